@@ -1,0 +1,204 @@
+"""Python binding of libgdn, the MI355X (gfx950) GDN token-mixer library.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libgdn.so`` (built in-tree by ``gated_deltanet_token_amd.build``), reached
+through its C ABI (``include/gdn.h``).  PyTorch supplies device memory and
+streams.  There is no fallback: importing this package without the built
+library raises ``ImportError``.
+
+bf16 tensors are ``torch.bfloat16``; token rows may be strided views (the
+last dimension must be contiguous).  Calls are asynchronous on the current
+torch stream unless ``stream`` is given.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK, GDN_ERR_INVALID, GDN_ERR_UNSUPPORTED, GDN_ERR_CAPACITY, GDN_ERR_HIP = 0, -1, -2, -3, -4
+CONV_CHUNK_TOKENS = 8
+CONV_WIDTH = 4
+
+# every entry point declared in include/gdn.h
+EXPORTS = ("gdn_last_error", "gdn_build_conv_chunks", "gdn_causal_conv1d_varlen",
+           "gdn_causal_conv1d_update", "gdn_fused_recurrent_decode")
+
+
+class GDNError(RuntimeError):
+    def __init__(self, code, func, message):
+        super().__init__("%s failed (%d): %s" % (func, code, message))
+        self.code = code
+
+
+def _bind(path):
+    lib = ctypes.CDLL(path)
+    P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.gdn_last_error.argtypes = []
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_build_conv_chunks.argtypes = [P, i32, P, i32, P]
+    lib.gdn_causal_conv1d_varlen.argtypes = [P, i64, P, P, P, i32, P, P, P, P, i32, P, i64,
+                                             i32, i32, i32, i32, i32, P]
+    lib.gdn_causal_conv1d_update.argtypes = [P, i64, P, P, P, i32, P, P, i64, i32, i32, i32, i32, P]
+    lib.gdn_fused_recurrent_decode.argtypes = [P, i64, P, i64, P, i64, P, P, P, i32, P, P, P, P, i64,
+                                               i32, i32, i32, i32, i32, i32, f32, i32, P]
+    for name in EXPORTS[1:]:
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+def _hip_runtimes():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libgdn.so is not built (%s); run python -m gated_deltanet_token_amd.build"
+                      % LIB_PATH)
+# torch's HIP runtime must be the process's only one: load it first so that
+# libgdn's libamdhip64.so.7 dependency resolves to it (by soname)
+import torch  # noqa: E402,F401
+
+lib = _bind(LIB_PATH)
+if len(_hip_runtimes()) > 1:
+    raise ImportError("two HIP runtimes are loaded (%s); libgdn must share torch's"
+                      % ", ".join(_hip_runtimes()))
+
+
+def _check(rc, func):
+    if rc != GDN_OK:
+        raise GDNError(rc, func, lib.gdn_last_error().decode())
+
+
+# ---------------------------------------------------------------------------
+# host call
+# ---------------------------------------------------------------------------
+
+def gdn_build_conv_chunks(query_start_loc_host) -> np.ndarray:
+    """Exact (sequence, 8-token chunk) descriptors as an int32 [n, 2] array
+    (layout of ``gdn_conv_chunk``), built on the host."""
+    qsl = np.ascontiguousarray(np.asarray(query_start_loc_host), dtype=np.int32)
+    ns = qsl.size - 1
+    n = ctypes.c_int32(0)
+    rc = lib.gdn_build_conv_chunks(qsl.ctypes.data, ns, None, 0, ctypes.byref(n))
+    if rc not in (GDN_OK, GDN_ERR_CAPACITY):
+        _check(rc, "gdn_build_conv_chunks")
+    out = np.empty((max(n.value, 1), 2), np.int32)
+    _check(lib.gdn_build_conv_chunks(qsl.ctypes.data, ns, out.ctypes.data, n.value, ctypes.byref(n)),
+           "gdn_build_conv_chunks")
+    return out[: n.value]
+
+
+# ---------------------------------------------------------------------------
+# GPU calls (torch tensors on the current HIP device)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _rows(t, name):
+    """Token stride (elements) of a 2-D tensor with a contiguous last dim."""
+    if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1):
+        raise ValueError("%s must be 2-D with contiguous rows" % name)
+    return t.stride(0) if t.size(0) > 1 else max(t.stride(0), t.size(1))
+
+
+def _heads(t, name):
+    """Token stride of a [T][H][d] tensor whose heads are packed."""
+    if t.dim() != 3 or t.stride(2) != 1 or (t.size(1) > 1 and t.stride(1) != t.size(2)):
+        raise ValueError("%s must be [T][H][d] with packed heads" % name)
+    return t.stride(0) if t.size(0) > 1 else max(t.stride(0), t.size(1) * t.size(2))
+
+
+def _dtype(t, dt, name):
+    if t is not None and t.dtype != dt:
+        raise TypeError("%s must be %s, got %s" % (name, dt, t.dtype))
+
+
+def gdn_causal_conv1d_varlen(x, weight, bias, conv_state, query_start_loc, state_indices,
+                             has_initial_state, chunks, y, silu=True, stream=None):
+    """Varlen causal conv (width 4) over packed tokens; see gdn.h.
+
+    x, y: bf16 [T][C] (strided rows allowed); weight bf16 [C][4]; bias bf16
+    [C] or None; conv_state bf16 [slots][3][C]; query_start_loc int32 [S+1];
+    state_indices int32 [S]; has_initial_state uint8 [S] or None; chunks
+    int32 [n][2] device tensor from gdn_build_conv_chunks (or None).
+    """
+    torch = _torch()
+    for t, n in ((x, "x"), (weight, "weight"), (bias, "bias"), (conv_state, "conv_state"), (y, "y")):
+        _dtype(t, torch.bfloat16, n)
+    _dtype(query_start_loc, torch.int32, "query_start_loc")
+    _dtype(state_indices, torch.int32, "state_indices")
+    _dtype(has_initial_state, torch.uint8, "has_initial_state")
+    _dtype(chunks, torch.int32, "chunks")
+    T, C = x.shape
+    n_chunks = 0 if chunks is None else chunks.shape[0]
+    rc = lib.gdn_causal_conv1d_varlen(
+        _ptr(x), _rows(x, "x"), _ptr(weight), _ptr(bias), _ptr(conv_state), conv_state.shape[0],
+        _ptr(query_start_loc), _ptr(state_indices), _ptr(has_initial_state),
+        _ptr(chunks) if n_chunks else None, n_chunks, _ptr(y), _rows(y, "y"),
+        query_start_loc.numel() - 1, T, C, weight.shape[1], int(bool(silu)), _stream(stream))
+    _check(rc, "gdn_causal_conv1d_varlen")
+
+
+def gdn_causal_conv1d_update(x, weight, bias, conv_state, state_indices, y, silu=True, stream=None):
+    """Single-token conv update (decode); see gdn.h."""
+    torch = _torch()
+    for t, n in ((x, "x"), (weight, "weight"), (bias, "bias"), (conv_state, "conv_state"), (y, "y")):
+        _dtype(t, torch.bfloat16, n)
+    _dtype(state_indices, torch.int32, "state_indices")
+    B, C = x.shape
+    rc = lib.gdn_causal_conv1d_update(
+        _ptr(x), _rows(x, "x"), _ptr(weight), _ptr(bias), _ptr(conv_state), conv_state.shape[0],
+        _ptr(state_indices), _ptr(y), _rows(y, "y"), B, C, weight.shape[1], int(bool(silu)),
+        _stream(stream))
+    _check(rc, "gdn_causal_conv1d_update")
+
+
+def gdn_fused_recurrent_decode(q, k, v, g, beta, state, state_indices, o, query_start_loc=None,
+                               has_initial_state=None, scale=1.0, qk_l2norm=True, stream=None):
+    """Gated delta rule over packed tokens; see gdn.h.
+
+    q, k: bf16 [T][HK][dk]; v: bf16 [T][HV][dv] (token rows may be strided
+    views of one wider activation); g, beta: fp32 [T][HV]; state: fp32
+    [slots][HV][dv][dk] (in place); o: bf16 [T][HV][dv]; query_start_loc
+    int32 [S+1] or None (one token per sequence, S = T).
+    """
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _dtype(t, torch.bfloat16, n)
+    for t, n in ((g, "g"), (beta, "beta"), (state, "state")):
+        _dtype(t, torch.float32, n)
+    _dtype(state_indices, torch.int32, "state_indices")
+    _dtype(query_start_loc, torch.int32, "query_start_loc")
+    _dtype(has_initial_state, torch.uint8, "has_initial_state")
+    if not (g.is_contiguous() and beta.is_contiguous() and state.is_contiguous()):
+        raise ValueError("g, beta and state must be contiguous")
+    T, HK, dk = q.shape
+    HV, dv = v.shape[1], v.shape[2]
+    S = state_indices.numel()
+    rc = lib.gdn_fused_recurrent_decode(
+        _ptr(q), _heads(q, "q"), _ptr(k), _heads(k, "k"), _ptr(v), _heads(v, "v"), _ptr(g),
+        _ptr(beta), _ptr(state), state.shape[0], _ptr(query_start_loc), _ptr(state_indices),
+        _ptr(has_initial_state), _ptr(o), _heads(o, "o"), S, T, HK, HV, dk, dv, float(scale),
+        int(bool(qk_l2norm)), _stream(stream))
+    _check(rc, "gdn_fused_recurrent_decode")

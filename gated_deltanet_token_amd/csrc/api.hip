@@ -1,0 +1,164 @@
+// C-ABI entry points of libgdn: host-side argument validation, the chunk
+// descriptor builder, and kernel launches on the caller's stream.  Every
+// check runs before anything is enqueued; a failing call enqueues nothing.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+#define GDN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return GDN_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// byte range of a strided row buffer [rows][stride] whose rows use `cols`
+// elements of `elem` bytes
+struct Span {
+    uintptr_t lo, hi;
+};
+Span row_span(const void *p, int64_t rows, int64_t stride, int64_t cols, int64_t elem) {
+    const uintptr_t lo = (uintptr_t)p;
+    if (rows <= 0 || cols <= 0) return {lo, lo};
+    return {lo, lo + (uintptr_t)(((rows - 1) * stride + cols) * elem)};
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int check_conv_common(const void *x, int64_t x_stride, const void *weight, const void *bias,
+                      const void *conv_state, int32_t num_slots, const void *y, int64_t y_stride,
+                      int32_t rows, int32_t channels, int32_t width) {
+    if (!x || !weight || !conv_state || !y) return fail(GDN_ERR_INVALID, "x, weight, conv_state and y are required");
+    if (rows < 0 || channels <= 0) return fail(GDN_ERR_INVALID, "negative token count or non-positive channels");
+    if (num_slots < 1) return fail(GDN_ERR_INVALID, "num_slots must be >= 1");
+    if (width != GDN_CONV_WIDTH) return fail(GDN_ERR_UNSUPPORTED, "conv width %d: only 4 is implemented", width);
+    if (x_stride < channels || y_stride < channels) return fail(GDN_ERR_INVALID, "row stride smaller than channels");
+    if (channels % 8 || x_stride % 8 || y_stride % 8)
+        return fail(GDN_ERR_UNSUPPORTED, "channels and strides must be multiples of 8 elements");
+    if (!aligned16(x) || !aligned16(y) || !aligned16(weight) || !aligned16(conv_state) ||
+        (bias && !aligned16(bias)))
+        return fail(GDN_ERR_UNSUPPORTED, "x, y, weight, bias and conv_state must be 16-byte aligned");
+    if (overlap(row_span(x, rows, x_stride, channels, 2), row_span(y, rows, y_stride, channels, 2)))
+        return fail(GDN_ERR_INVALID, "y overlaps x");
+    return ok();
+}
+
+}  // namespace
+
+GDN_EXPORT const char *gdn_last_error(void) { return g_err; }
+
+GDN_EXPORT int gdn_build_conv_chunks(const int32_t *qsl_host, int32_t num_seqs, gdn_conv_chunk *out_host,
+                                     int32_t capacity, int32_t *n_out) {
+    if (!qsl_host || !n_out) return fail(GDN_ERR_INVALID, "qsl_host and n_out are required");
+    if (num_seqs < 0 || capacity < 0) return fail(GDN_ERR_INVALID, "negative num_seqs or capacity");
+    if (capacity > 0 && !out_host) return fail(GDN_ERR_INVALID, "out_host is NULL with capacity > 0");
+    int64_t n = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int64_t len = (int64_t)qsl_host[s + 1] - qsl_host[s];
+        if (len < 0) return fail(GDN_ERR_INVALID, "query_start_loc decreases at sequence %d", s);
+        const int64_t chunks = (len + GDN_CONV_CHUNK_TOKENS - 1) / GDN_CONV_CHUNK_TOKENS;
+        for (int64_t c = 0; c < chunks; ++c, ++n) {
+            if (n < capacity) out_host[n] = gdn_conv_chunk{s, (int32_t)c};
+        }
+        if (n > INT32_MAX) return fail(GDN_ERR_INVALID, "descriptor count overflows int32");
+    }
+    *n_out = (int32_t)n;
+    if (n > capacity) return fail(GDN_ERR_CAPACITY, "%lld descriptors needed, capacity %d", (long long)n, capacity);
+    return ok();
+}
+
+GDN_EXPORT int gdn_causal_conv1d_varlen(const gdn_bf16 *x, int64_t x_stride, const gdn_bf16 *weight,
+                                        const gdn_bf16 *bias, gdn_bf16 *conv_state, int32_t num_slots,
+                                        const int32_t *query_start_loc, const int32_t *state_indices,
+                                        const uint8_t *has_initial_state, const gdn_conv_chunk *chunks,
+                                        int32_t n_chunks, gdn_bf16 *y, int64_t y_stride, int32_t num_seqs,
+                                        int32_t num_tokens, int32_t channels, int32_t width, int32_t silu,
+                                        void *stream) {
+    int rc = check_conv_common(x, x_stride, weight, bias, conv_state, num_slots, y, y_stride, num_tokens,
+                               channels, width);
+    if (rc) return rc;
+    if (num_seqs < 0 || n_chunks < 0) return fail(GDN_ERR_INVALID, "negative num_seqs or n_chunks");
+    if ((chunks == nullptr) != (n_chunks == 0))
+        return fail(GDN_ERR_INVALID, "chunks and n_chunks must be given together");
+    if (n_chunks == 0) return ok();
+    if (!query_start_loc || !state_indices) return fail(GDN_ERR_INVALID, "query_start_loc and state_indices are required");
+    if (num_seqs == 0 || num_tokens == 0) return fail(GDN_ERR_INVALID, "descriptors given for an empty batch");
+    if ((int64_t)n_chunks > (int64_t)num_tokens)
+        return fail(GDN_ERR_INVALID, "more descriptors (%d) than tokens (%d)", n_chunks, num_tokens);
+    gdn::ConvVarlenArgs a{x, x_stride, weight, bias, conv_state, query_start_loc, state_indices,
+                          has_initial_state, chunks, n_chunks, y, y_stride, channels, silu};
+    return hip_status(gdn::launch_conv_varlen(a, (hipStream_t)stream), "conv varlen launch");
+}
+
+GDN_EXPORT int gdn_causal_conv1d_update(const gdn_bf16 *x, int64_t x_stride, const gdn_bf16 *weight,
+                                        const gdn_bf16 *bias, gdn_bf16 *conv_state, int32_t num_slots,
+                                        const int32_t *state_indices, gdn_bf16 *y, int64_t y_stride,
+                                        int32_t batch, int32_t channels, int32_t width, int32_t silu,
+                                        void *stream) {
+    int rc = check_conv_common(x, x_stride, weight, bias, conv_state, num_slots, y, y_stride, batch,
+                               channels, width);
+    if (rc) return rc;
+    if (batch == 0) return ok();
+    if (!state_indices) return fail(GDN_ERR_INVALID, "state_indices is required");
+    gdn::ConvUpdateArgs a{x, x_stride, weight, bias, conv_state, state_indices, y, y_stride, batch, channels, silu};
+    return hip_status(gdn::launch_conv_update(a, (hipStream_t)stream), "conv update launch");
+}
+
+GDN_EXPORT int gdn_fused_recurrent_decode(const gdn_bf16 *q, int64_t q_stride, const gdn_bf16 *k, int64_t k_stride,
+                                          const gdn_bf16 *v, int64_t v_stride, const float *g, const float *beta,
+                                          float *state, int32_t num_slots, const int32_t *query_start_loc,
+                                          const int32_t *state_indices, const uint8_t *has_initial_state,
+                                          gdn_bf16 *o, int64_t o_stride, int32_t num_seqs, int32_t num_tokens,
+                                          int32_t num_k_heads, int32_t num_v_heads, int32_t head_k_dim,
+                                          int32_t head_v_dim, float scale, int32_t qk_l2norm, void *stream) {
+    if (!q || !k || !v || !g || !beta || !state || !state_indices || !o)
+        return fail(GDN_ERR_INVALID, "q, k, v, g, beta, state, state_indices and o are required");
+    if (num_seqs < 0 || num_tokens < 0) return fail(GDN_ERR_INVALID, "negative num_seqs or num_tokens");
+    if (num_slots < 1) return fail(GDN_ERR_INVALID, "num_slots must be >= 1");
+    if (num_k_heads <= 0 || num_v_heads <= 0 || num_v_heads % num_k_heads)
+        return fail(GDN_ERR_INVALID, "num_v_heads must be a positive multiple of num_k_heads");
+    if (head_k_dim != 16 && head_k_dim != 32 && head_k_dim != 64 && head_k_dim != 128)
+        return fail(GDN_ERR_UNSUPPORTED, "head_k_dim %d: supported 16, 32, 64, 128", head_k_dim);
+    if (head_v_dim <= 0 || head_v_dim % 8 || head_v_dim > 256)
+        return fail(GDN_ERR_UNSUPPORTED, "head_v_dim %d: must be a multiple of 8 up to 256", head_v_dim);
+    const int64_t qk_w = (int64_t)num_k_heads * head_k_dim, v_w = (int64_t)num_v_heads * head_v_dim;
+    if (q_stride < qk_w || k_stride < qk_w || v_stride < v_w || o_stride < v_w)
+        return fail(GDN_ERR_INVALID, "a token stride is smaller than its row of heads");
+    if (q_stride % 8 || k_stride % 8 || v_stride % 8 || o_stride % 8)
+        return fail(GDN_ERR_UNSUPPORTED, "token strides must be multiples of 8 elements");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state))
+        return fail(GDN_ERR_UNSUPPORTED, "q, k, v, o and state must be 16-byte aligned");
+    if (!query_start_loc && num_tokens != num_seqs)
+        return fail(GDN_ERR_INVALID, "without query_start_loc num_tokens must equal num_seqs");
+    const Span os = row_span(o, num_tokens, o_stride, v_w, 2);
+    if (overlap(os, row_span(q, num_tokens, q_stride, qk_w, 2)) ||
+        overlap(os, row_span(k, num_tokens, k_stride, qk_w, 2)) ||
+        overlap(os, row_span(v, num_tokens, v_stride, v_w, 2)))
+        return fail(GDN_ERR_INVALID, "o overlaps q, k or v");
+    if (num_seqs == 0 || num_tokens == 0) return ok();
+    gdn::RecurrentArgs a{q, q_stride, k, k_stride, v, v_stride, g, beta, state, query_start_loc, state_indices,
+                         has_initial_state, o, o_stride, num_seqs, num_k_heads, num_v_heads, head_k_dim,
+                         head_v_dim, scale, qk_l2norm};
+    return hip_status(gdn::launch_recurrent(a, (hipStream_t)stream), "recurrent launch");
+}

@@ -1,0 +1,71 @@
+// Internal launch interface between the C-ABI entry points (api.hip) and the
+// kernel files.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+struct ConvVarlenArgs {
+    const uint16_t *x;
+    int64_t x_stride;
+    const uint16_t *weight;
+    const uint16_t *bias;
+    uint16_t *conv_state;
+    const int32_t *qsl;
+    const int32_t *state_indices;
+    const uint8_t *has_init;
+    const gdn_conv_chunk *chunks;
+    int n_chunks;
+    uint16_t *y;
+    int64_t y_stride;
+    int channels;
+    int silu;
+};
+
+struct ConvUpdateArgs {
+    const uint16_t *x;
+    int64_t x_stride;
+    const uint16_t *weight;
+    const uint16_t *bias;
+    uint16_t *conv_state;
+    const int32_t *state_indices;
+    uint16_t *y;
+    int64_t y_stride;
+    int batch;
+    int channels;
+    int silu;
+};
+
+struct RecurrentArgs {
+    const uint16_t *q;
+    int64_t q_stride;
+    const uint16_t *k;
+    int64_t k_stride;
+    const uint16_t *v;
+    int64_t v_stride;
+    const float *g;
+    const float *beta;
+    float *state;
+    const int32_t *qsl;          // nullptr: one token per sequence
+    const int32_t *state_indices;
+    const uint8_t *has_init;     // nullptr: all have an initial state
+    uint16_t *o;
+    int64_t o_stride;
+    int num_seqs;
+    int num_k_heads;
+    int num_v_heads;
+    int dk;
+    int dv;
+    float scale;
+    int l2norm;
+};
+
+hipError_t launch_conv_varlen(const ConvVarlenArgs &a, hipStream_t stream);
+hipError_t launch_conv_update(const ConvUpdateArgs &a, hipStream_t stream);
+hipError_t launch_recurrent(const RecurrentArgs &a, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,220 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet (GDN) token-mixer library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Four calls form the layer's data-parallel hot path:
+ *
+ *   gdn_build_conv_chunks       host: exact (sequence, 8-token chunk) list
+ *   gdn_causal_conv1d_varlen    GPU: width-4 causal conv over packed prefill
+ *   gdn_causal_conv1d_update    GPU: single-token conv for decode
+ *   gdn_fused_recurrent_decode  GPU: gated delta rule over packed tokens
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - bf16 values travel as raw 16-bit patterns (gdn_bf16).  fp32 -> bf16
+ *   rounding is round-to-nearest-even.  Arithmetic is fp32.
+ * - Unless marked "host", a pointer is a device pointer (HBM of the current
+ *   HIP device).  The caller owns every buffer.  The library never allocates,
+ *   frees or caches device memory or pointers, holds no global mutable state
+ *   and may be called from several threads (each on its own buffers).
+ * - GPU calls validate their arguments on the host, then enqueue kernels on
+ *   `stream` (a hipStream_t; NULL = the default stream) and return without
+ *   waiting.  A call that returns an error enqueued nothing.
+ * - "Stride" arguments count elements, not bytes, between consecutive token
+ *   rows.  Within a row, channels (or heads, then head elements) are packed.
+ * - Vector-access contract: bf16 row pointers and strides are multiples of
+ *   8 elements (16 bytes); fp32 state pointers are 16-byte aligned.
+ * - Sequences are packed back to back.  query_start_loc[s] .. [s+1] is the
+ *   token range of sequence s; it must be non-decreasing with
+ *   query_start_loc[0] == 0 (device-side preconditions are documented, not
+ *   checked).  state_indices[s] selects the state slot of sequence s; a
+ *   negative index marks padding: that sequence is skipped, its outputs and
+ *   every slot are left untouched.  Slots used in one call must be distinct.
+ *
+ * Return values: GDN_OK or a negative gdn_status; gdn_last_error() then
+ * describes the failure (thread-local, valid until the thread's next call).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t gdn_bf16;
+
+/* Tokens per conv program: one descriptor covers tokens
+ * [qsl[seq] + 8*chunk, min(qsl[seq] + 8*chunk + 8, qsl[seq+1])). */
+#define GDN_CONV_CHUNK_TOKENS 8
+/* The only conv width the library implements. */
+#define GDN_CONV_WIDTH 4
+
+typedef struct gdn_conv_chunk {
+    int32_t seq;    /* sequence index into query_start_loc */
+    int32_t chunk;  /* 8-token chunk index within that sequence */
+} gdn_conv_chunk;
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_INVALID = -1,      /* NULL pointer, bad count, bad pair, aliasing */
+    GDN_ERR_UNSUPPORTED = -2,  /* width != 4, misaligned, unsupported head dim */
+    GDN_ERR_CAPACITY = -3,     /* descriptor buffer too small */
+    GDN_ERR_HIP = -4           /* the HIP runtime reported an error */
+} gdn_status;
+
+/* Text of the last error on the calling thread ("" after a success). */
+const char *gdn_last_error(void);
+
+/*
+ * gdn_build_conv_chunks -- host only, synchronous.
+ *
+ * Source: page "perf(gdn): dispatch exact causal-conv chunks", section "What
+ * changed": the conv is dispatched as one program per exact (sequence,
+ * 8-token chunk) pair; the list is built once per engine step, uploaded once
+ * and reused by every GDN layer of the step.
+ *
+ * For s = 0 .. num_seqs-1 and c = 0 .. ceil(L_s / 8) - 1 (L_s =
+ * qsl_host[s+1] - qsl_host[s]) appends {s, c}: sequences in order, chunks
+ * ascending; empty sequences contribute nothing.
+ *
+ *   qsl_host   host, int32 [num_seqs + 1], non-decreasing (checked)
+ *   out_host   host, gdn_conv_chunk [capacity]; may be NULL if capacity == 0
+ *   n_out      host, receives the number of descriptors needed
+ *
+ * Errors: GDN_ERR_INVALID (NULL qsl_host/n_out, num_seqs < 0, capacity < 0,
+ * decreasing qsl, count overflow); GDN_ERR_CAPACITY when the list does not
+ * fit: *n_out then holds the required count and out_host[0 .. capacity) holds
+ * the first descriptors.  Pass capacity 0 to query the count.
+ */
+int gdn_build_conv_chunks(const int32_t *qsl_host, int32_t num_seqs,
+                          gdn_conv_chunk *out_host, int32_t capacity, int32_t *n_out);
+
+/*
+ * gdn_causal_conv1d_varlen -- depthwise causal conv1d over packed prefill
+ * tokens, width 4, optional SiLU, per-sequence carried state.
+ *
+ * Sources: page "perf(gdn): dispatch exact causal-conv chunks", section "What
+ * changed" (one program per exact chunk descriptor; the descriptor is
+ * optional and its (buffer, count) pair is validated together, reviewer
+ * comment on the same page); page "RTX 5070 Ti: close Qwen3.5-4B TTFT, TPOT,
+ * and VRAM gaps vs vLLM", section "Existing evidence" (width-4 conv).
+ *
+ * For each sequence s with slot = state_indices[s] >= 0, tokens [a, a+L):
+ *   window e = h || x[a .. a+L), h = conv_state[slot] if has_initial_state[s]
+ *             else 3 zero rows (oldest first)
+ *   y[a+p][c] = act(bias[c] + sum_{j<4} weight[c][j] * e[p+j][c])
+ *             (weight[c][3] multiplies the current token; act = SiLU if silu)
+ *   conv_state[slot] <- e[L .. L+3)   (the three newest window rows)
+ *
+ *   x                 bf16 [num_tokens][x_stride], channels [0, channels)
+ *   weight            bf16 [channels][4]
+ *   bias              bf16 [channels], or NULL for no bias
+ *   conv_state        bf16 [num_slots][3][channels], read and written in place
+ *   query_start_loc   int32 [num_seqs + 1]
+ *   state_indices     int32 [num_seqs]
+ *   has_initial_state uint8 [num_seqs], or NULL (= every sequence has one)
+ *   chunks, n_chunks  descriptors from gdn_build_conv_chunks on the same
+ *                     query_start_loc, copied to the device.  Both NULL/0 is a
+ *                     valid empty call; exactly one of them set is an error.
+ *   y                 bf16 [num_tokens][y_stride]; must not overlap x
+ *
+ * Errors: GDN_ERR_INVALID (required pointer NULL, negative count,
+ * (chunks == NULL) != (n_chunks == 0), stride < channels, x and y overlap,
+ * num_slots < 1); GDN_ERR_UNSUPPORTED (width != 4, channels % 8, strides or
+ * pointers off the 16-byte contract); GDN_ERR_HIP (launch failure).
+ */
+int gdn_causal_conv1d_varlen(const gdn_bf16 *x, int64_t x_stride,
+                             const gdn_bf16 *weight, const gdn_bf16 *bias,
+                             gdn_bf16 *conv_state, int32_t num_slots,
+                             const int32_t *query_start_loc,
+                             const int32_t *state_indices,
+                             const uint8_t *has_initial_state,
+                             const gdn_conv_chunk *chunks, int32_t n_chunks,
+                             gdn_bf16 *y, int64_t y_stride,
+                             int32_t num_seqs, int32_t num_tokens, int32_t channels,
+                             int32_t width, int32_t silu, void *stream);
+
+/*
+ * gdn_causal_conv1d_update -- the same conv for one new token per sequence
+ * (decode): row b uses slot state_indices[b] (negative: row skipped).
+ *
+ *   y[b][c] = act(bias[c] + sum_{j<3} weight[c][j] * conv_state[slot][j][c]
+ *                 + weight[c][3] * x[b][c])
+ *   conv_state[slot] <- (conv_state[slot][1], conv_state[slot][2], x[b])
+ *
+ * Identical arithmetic to gdn_causal_conv1d_varlen, so a sequence advanced
+ * by this call gives bit-identical outputs to the varlen call on the whole
+ * sequence.  Layouts as above with num_tokens = batch.
+ *
+ * Errors: as gdn_causal_conv1d_varlen (minus the descriptor pair).
+ */
+int gdn_causal_conv1d_update(const gdn_bf16 *x, int64_t x_stride,
+                             const gdn_bf16 *weight, const gdn_bf16 *bias,
+                             gdn_bf16 *conv_state, int32_t num_slots,
+                             const int32_t *state_indices,
+                             gdn_bf16 *y, int64_t y_stride,
+                             int32_t batch, int32_t channels, int32_t width,
+                             int32_t silu, void *stream);
+
+/*
+ * gdn_fused_recurrent_decode -- the gated delta rule, fused per (sequence,
+ * v-head), token by token, over packed tokens (decode: one token each).
+ *
+ * Sources: the fused GDN decode with a register-resident state named on page
+ * "RTX 5070 Ti: close Qwen3.5-4B TTFT, TPOT, and VRAM gaps vs vLLM", section
+ * "Existing evidence"; the rule itself from Yang, Kautz, Hatamizadeh, "Gated
+ * Delta Networks: Improving Mamba2 with Delta Rule" (ICLR 2025).
+ *
+ * For each sequence s with slot = state_indices[s] >= 0 and v-head h (q/k
+ * head hk = h / (num_v_heads / num_k_heads)):
+ *   S = has_initial_state[s] ? state[slot][h] : 0      (dv x dk, fp32)
+ *   for each token t of s:
+ *     qh, kh = q[t][hk], k[t][hk], each divided by sqrt(sum x^2 + 1e-6)
+ *              when qk_l2norm != 0
+ *     a = exp(g[t][h]),  b = beta[t][h]
+ *     S = a * S * (I - b kh kh^T) + b v[t][h] kh^T
+ *     o[t][h] = scale * S qh
+ *   state[slot][h] = S
+ *
+ *   q, k     bf16, token t head j at q + t*q_stride + j*head_k_dim
+ *   v        bf16, token t head h at v + t*v_stride + h*head_v_dim
+ *            (q, k and v may be column views of one conv output row)
+ *   g, beta  fp32 [num_tokens][num_v_heads]  (g = log decay)
+ *   state    fp32 [num_slots][num_v_heads][head_v_dim][head_k_dim], in place;
+ *            row i (one v channel) is contiguous along head_k_dim
+ *   query_start_loc  int32 [num_seqs + 1], or NULL: one token per sequence
+ *            (then num_tokens == num_seqs and token s belongs to sequence s)
+ *   o        bf16, token t head h at o + t*o_stride + h*head_v_dim
+ *
+ * Launch shape: with query_start_loc == NULL the call is laid out for
+ * bandwidth (every state row streamed once); with it, for per-token
+ * latency.  Both shapes do identical per-token arithmetic, so splitting a
+ * sequence across calls gives bit-identical results.
+ *
+ * Errors: GDN_ERR_INVALID (required pointer NULL, negative count,
+ * num_v_heads % num_k_heads, strides too small, num_tokens != num_seqs
+ * without query_start_loc, o overlapping q/k/v); GDN_ERR_UNSUPPORTED
+ * (head_k_dim not in {16, 32, 64, 128}, head_v_dim not a positive multiple
+ * of 8 up to 256, alignment contract); GDN_ERR_HIP.
+ */
+int gdn_fused_recurrent_decode(const gdn_bf16 *q, int64_t q_stride,
+                               const gdn_bf16 *k, int64_t k_stride,
+                               const gdn_bf16 *v, int64_t v_stride,
+                               const float *g, const float *beta,
+                               float *state, int32_t num_slots,
+                               const int32_t *query_start_loc,
+                               const int32_t *state_indices,
+                               const uint8_t *has_initial_state,
+                               gdn_bf16 *o, int64_t o_stride,
+                               int32_t num_seqs, int32_t num_tokens,
+                               int32_t num_k_heads, int32_t num_v_heads,
+                               int32_t head_k_dim, int32_t head_v_dim,
+                               float scale, int32_t qk_l2norm, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,151 @@
+"""CPU checks of the C-ABI library: it loads, exports every call declared
+in include/gdn.h, builds chunk descriptors bit-exactly like the oracle, and
+rejects each invalid argument with its documented status before touching
+the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gated_deltanet_token_amd as gdn
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INV, UNS, CAP = gdn.GDN_ERR_INVALID, gdn.GDN_ERR_UNSUPPORTED, gdn.GDN_ERR_CAPACITY
+
+
+def declared_calls():
+    text = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_call():
+    names = declared_calls()
+    assert set(names) == set(gdn.EXPORTS)
+    for n in names:
+        assert hasattr(gdn.lib, n), n
+
+
+def _chunks_lib(qsl, capacity):
+    qsl = np.ascontiguousarray(qsl, np.int32)
+    out = (gdn_conv_chunk * max(capacity, 1))()
+    n = ctypes.c_int32(-1)
+    rc = gdn.lib.gdn_build_conv_chunks(qsl.ctypes.data, qsl.size - 1, out, capacity, ctypes.byref(n))
+    return rc, n.value, np.array([(c.seq, c.chunk) for c in out[:min(capacity, max(n.value, 0))]],
+                                 np.int32).reshape(-1, 2)
+
+
+class gdn_conv_chunk(ctypes.Structure):
+    _fields_ = [("seq", ctypes.c_int32), ("chunk", ctypes.c_int32)]
+
+
+def test_chunks_bit_exact_vs_oracle_random_and_edges():
+    r = np.random.default_rng(7)
+    cases = [[0], [0, 0], [0, 5, 18], [0, 1024, 2048], [0, 8, 16, 24], [0, 7, 7, 15, 16, 17]]
+    for _ in range(300):
+        S = int(r.integers(1, 40))
+        lens = r.integers(0, 40, S) * (r.random(S) < 0.9)
+        cases.append(np.concatenate([[0], np.cumsum(lens)]).tolist())
+    for qsl in cases:
+        ref = oracle.build_conv_chunks(qsl)
+        got = gdn.gdn_build_conv_chunks(qsl)
+        assert got.dtype == np.int32 and np.array_equal(got, ref), qsl
+
+
+def test_chunks_capacity_and_errors():
+    rc, n, got = _chunks_lib([0, 9, 9, 30], 2)
+    assert rc == CAP and n == 5 and np.array_equal(got, [[0, 0], [0, 1]])
+    rc, n, _ = _chunks_lib([0, 9, 9, 30], 0)
+    assert rc == CAP and n == 5
+    rc, n, got = _chunks_lib([0, 9, 9, 30], 5)
+    assert rc == 0 and n == 5
+    rc, _, _ = _chunks_lib([0, 5, 3], 10)
+    assert rc == INV and b"decreases" in gdn.lib.gdn_last_error()
+    n = ctypes.c_int32()
+    assert gdn.lib.gdn_build_conv_chunks(None, 1, None, 0, ctypes.byref(n)) == INV
+    q = np.array([0, 1], np.int32)
+    assert gdn.lib.gdn_build_conv_chunks(q.ctypes.data, -1, None, 0, ctypes.byref(n)) == INV
+    assert gdn.lib.gdn_build_conv_chunks(q.ctypes.data, 1, None, 4, ctypes.byref(n)) == INV
+
+
+# fake, well-aligned device addresses: validation never dereferences them and
+# every case below fails validation, so nothing is launched
+A = 0x10000000
+X, W, B, CS, QSL, IDX, HI, CH, Y = (A + i * 0x1000000 for i in range(9))
+
+
+def varlen(**kw):
+    a = dict(x=X, xs=8192, w=W, b=B, cs=CS, slots=64, qsl=QSL, idx=IDX, hi=HI, ch=CH, nch=256,
+             y=Y, ys=8192, S=2, T=2048, C=8192, K=4, silu=1)
+    a.update(kw)
+    return gdn.lib.gdn_causal_conv1d_varlen(a["x"], a["xs"], a["w"], a["b"], a["cs"], a["slots"], a["qsl"],
+                                            a["idx"], a["hi"], a["ch"], a["nch"], a["y"], a["ys"], a["S"],
+                                            a["T"], a["C"], a["K"], a["silu"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), INV), (dict(w=None), INV), (dict(cs=None), INV), (dict(y=None), INV),
+    (dict(qsl=None), INV), (dict(idx=None), INV),
+    (dict(ch=None), INV),                        # pair mismatch: count without buffer
+    (dict(nch=0), INV),                          # pair mismatch: buffer without count
+    (dict(nch=-1), INV), (dict(S=-1), INV), (dict(T=-1), INV), (dict(slots=0), INV),
+    (dict(xs=8000), INV), (dict(ys=100), INV), (dict(y=X), INV), (dict(y=X + 2 * 8192), INV),
+    (dict(nch=3000), INV), (dict(S=0), INV),
+    (dict(K=3), UNS), (dict(K=5), UNS), (dict(C=8190, xs=8190, ys=8190), UNS),
+    (dict(xs=8196), UNS), (dict(x=X + 2), UNS), (dict(b=B + 8), UNS), (dict(cs=CS + 4), UNS),
+])
+def test_conv_varlen_validation(kw, code):
+    assert varlen(**kw) == code, gdn.lib.gdn_last_error()
+    assert gdn.lib.gdn_last_error()
+
+
+def update(**kw):
+    a = dict(x=X, xs=8192, w=W, b=B, cs=CS, slots=64, idx=IDX, y=Y, ys=8192, B=32, C=8192, K=4, silu=1)
+    a.update(kw)
+    return gdn.lib.gdn_causal_conv1d_update(a["x"], a["xs"], a["w"], a["b"], a["cs"], a["slots"], a["idx"],
+                                            a["y"], a["ys"], a["B"], a["C"], a["K"], a["silu"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), INV), (dict(idx=None), INV), (dict(B=-1), INV), (dict(y=X), INV),
+    (dict(slots=0), INV), (dict(K=2), UNS), (dict(C=12, xs=16, ys=16), UNS), (dict(y=Y + 6), UNS),
+])
+def test_conv_update_validation(kw, code):
+    assert update(**kw) == code, gdn.lib.gdn_last_error()
+
+
+Q, K_, V, G, BE, ST, O = (A + i * 0x4000000 for i in range(7))
+
+
+def rec(**kw):
+    a = dict(q=Q, qs=2048, k=K_, ks=2048, v=V, vs=4096, g=G, b=BE, st=ST, slots=64, qsl=None, idx=IDX,
+             hi=None, o=O, os=4096, S=32, T=32, HK=16, HV=32, dk=128, dv=128, scale=1.0, norm=1)
+    a.update(kw)
+    return gdn.lib.gdn_fused_recurrent_decode(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["g"],
+                                              a["b"], a["st"], a["slots"], a["qsl"], a["idx"], a["hi"],
+                                              a["o"], a["os"], a["S"], a["T"], a["HK"], a["HV"], a["dk"],
+                                              a["dv"], a["scale"], a["norm"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INV), (dict(k=None), INV), (dict(v=None), INV), (dict(g=None), INV),
+    (dict(b=None), INV), (dict(st=None), INV), (dict(idx=None), INV), (dict(o=None), INV),
+    (dict(S=-1), INV), (dict(T=-2), INV), (dict(slots=0), INV), (dict(HV=24), INV), (dict(HK=0), INV),
+    (dict(qs=2000), INV), (dict(vs=4000), INV), (dict(os=1024), INV),
+    (dict(T=33), INV),                           # one token per sequence without qsl
+    (dict(o=V), INV),                            # o overlaps v
+    (dict(dk=96), UNS), (dict(dk=256), UNS), (dict(dv=100), UNS), (dict(dv=512), UNS),
+    (dict(qs=2052), UNS), (dict(q=Q + 8), UNS), (dict(st=ST + 4), UNS),
+])
+def test_recurrent_validation(kw, code):
+    assert rec(**kw) == code, gdn.lib.gdn_last_error()
+
+
+def test_error_text_cleared_on_success():
+    varlen(K=3)
+    assert gdn.lib.gdn_last_error()
+    gdn.gdn_build_conv_chunks([0, 4])
+    assert gdn.lib.gdn_last_error() == b""
