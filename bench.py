@@ -1,0 +1,343 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN token-mixer hot path on one MI355X.
+
+Workload (one bench "step"): the c32 engine-step trace -- 128 requests of
+1,024 prompt tokens and 128 output tokens, at most 32 running, 2,048-token
+chunked-prefill budget per engine step, FIFO admission (529 engine steps,
+147,328 tokens) -- pushed through ``--layers`` GDN layers.  Each layer has its
+own conv weights, conv_state pool and recurrent-state pool (64 slots each)
+and its own activations, so consecutive layers do not find each other's state
+in the 256 MB Infinity Cache, as in a model with several GDN layers.
+
+Per engine step: the host builds the exact (sequence, 8-token chunk)
+descriptors once (gdn_build_conv_chunks) and uploads them once; then for every
+layer: conv update for the decode rows, varlen conv for the prefill rows,
+the fused recurrence for the decodes and for the prefill chunks (q, k, v
+are column views of the conv output).  Inputs are resident in HBM before the
+timed region; every call goes through the C ABI on torch's current stream.
+
+Output: one JSON line.  ``value`` is GDN-layer tokens per second (tokens x
+layers / wall time).  ``roofline`` is for the kernel with the largest share
+of GPU time, timed with HIP events around each of its launches inside the
+timed region.  ``cpu_baseline`` is the fp64 oracle timed on this host on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN layer tokens/s + achieved HBM GB/s (% peak), c32 prefill & decode"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak
+
+C, HK, HV, D, K = 8192, 16, 32, 128, 4
+SLOTS = 64
+BUDGET = 2048
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-sample-requests", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (3 times) and exit: the "
+                         "reference kernel for scaling memory-traffic counters")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work per launch (what the method must move / compute)
+# ---------------------------------------------------------------------------
+
+def bytes_conv_varlen(tokens, seqs, seqs_with_init, n_chunks):
+    return (2 * tokens * C * 2                       # x read, y write
+            + seqs * 3 * C * 2 + seqs_with_init * 3 * C * 2   # slot write / read
+            + C * K * 2 + C * 2                      # weights, bias
+            + n_chunks * 8 + (seqs + 1) * 4 + seqs * 5)
+
+
+def bytes_conv_update(batch):
+    return batch * (2 * C * 2 + 2 * 3 * C * 2 + 4) + C * K * 2 + C * 2
+
+
+def bytes_recurrent(tokens, seqs_with_state_read, seqs):
+    state = D * D * 4 * HV
+    return (seqs_with_state_read * state + seqs * state          # state read, write
+            + tokens * ((2 * HK * D + HV * D) * 2 + HV * D * 2 + HV * 8))
+
+
+def flops_recurrent(tokens):
+    # per token and v-head: S k (2 d^2), the rank-1 update a S + c k^T (2 d^2),
+    # S q (2 d^2)
+    return 6.0 * tokens * HV * D * D
+
+
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(seed, n_req, seq_len):
+    import oracle
+    import synth
+    w, b = synth.trace_layer_weights(seed, 0)
+    elapsed = 0.0
+    for r in range(n_req):
+        x, g, beta = synth.trace_request_inputs(seed, 0, r, seq_len)
+        t0 = time.perf_counter()
+        y, _ = oracle.causal_conv1d_varlen(x, w, b, np.zeros((1, 3, C), np.uint16), [0, seq_len], [0], [0])
+        yb = oracle.round_bf16(y)
+        q = yb[:, :HK * D].reshape(seq_len, HK, D)
+        k = yb[:, HK * D:2 * HK * D].reshape(seq_len, HK, D)
+        v = yb[:, 2 * HK * D:].reshape(seq_len, HV, D)
+        oracle.gated_delta_rule(q, k, v, g, beta, np.zeros((1, HV, D, D)), [0], [0, seq_len], [0], 1.0, True)
+        elapsed += time.perf_counter() - t0
+    return {"value": n_req * seq_len / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d of the 128 requests, %d tokens each (1024 prompt + 127 decode forwards), "
+                      "one GDN layer, whole-sequence oracle passes (conv, bf16 rounding, gated delta "
+                      "rule); serial C in fp64; %.1f s" % (n_req, seq_len, elapsed)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (the GDN mixer shards by sequence or head "
+              "group with no exchange inside the path); --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_token_amd as gdn
+    import synth
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+        return
+
+    lib = gdn.lib
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    trace = synth.engine_trace_schedule(args.seed)
+    steps = trace.steps
+    _, offs = synth.trace_step_rows(trace)
+    T_all = int(offs[-1])
+    L = args.layers
+
+    # ---- per-step metadata (host and device), built before the timed region
+    dec_idx, pf_qsl, pf_idx, pf_hi, n_chunks = [], [], [], [], []
+    for st in steps:
+        dec_idx.append(np.array([s for (_r, _p, s) in st.decodes], np.int32))
+        lens = [n for (_r, _p0, n, _s, _h) in st.prefills]
+        pf_qsl.append(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+        pf_idx.append(np.array([s for (_r, _p0, _n, s, _h) in st.prefills], np.int32))
+        pf_hi.append(np.array([h for (_r, _p0, _n, _s, h) in st.prefills], np.uint8))
+        n_chunks.append(sum((n + 7) // 8 for n in lens))
+
+    def pack(arrs, dtype):
+        offs_ = np.concatenate([[0], np.cumsum([len(a) for a in arrs])]).astype(np.int64)
+        flat = np.concatenate(arrs).astype(dtype) if offs_[-1] else np.zeros(1, dtype)
+        t = torch.from_numpy(flat).to(dev)
+        return t, offs_
+
+    dec_idx_d, dec_off = pack(dec_idx, np.int32)
+    qsl_d, qsl_off = pack(pf_qsl, np.int32)
+    pidx_d, pidx_off = pack(pf_idx, np.int32)
+    phi_d, phi_off = pack(pf_hi, np.uint8)
+    ch_off = np.concatenate([[0], np.cumsum(n_chunks)]).astype(np.int64)
+    ch_host = torch.zeros(int(ch_off[-1]) * 2, dtype=torch.int32, pin_memory=True)
+    ch_dev = torch.zeros(int(ch_off[-1]) * 2, dtype=torch.int32, device=dev)
+    qsl_host = [np.ascontiguousarray(q) for q in pf_qsl]
+
+    # ---- per-layer weights, pools and activations (seeded, on the device)
+    layers = []
+    for li in range(L):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1000 * args.seed + li)
+        x = torch.empty(T_all, C, dtype=torch.bfloat16, device=dev)
+        for a in range(0, T_all, 16384):
+            e = min(T_all, a + 16384)
+            x[a:e] = torch.randn(e - a, C, generator=gen, device=dev).to(torch.bfloat16)
+        g = -torch.nn.functional.softplus(torch.randn(T_all, HV, generator=gen, device=dev))
+        beta = torch.sigmoid(torch.randn(T_all, HV, generator=gen, device=dev))
+        w = (0.5 * torch.randn(C, K, generator=gen, device=dev)).to(torch.bfloat16)
+        b = (0.1 * torch.randn(C, generator=gen, device=dev)).to(torch.bfloat16)
+        layers.append(dict(
+            x=x, g=g.contiguous(), beta=beta.contiguous(), w=w, b=b,
+            cs=torch.zeros(SLOTS, 3, C, dtype=torch.bfloat16, device=dev),
+            state=torch.zeros(SLOTS, HV, D, D, dtype=torch.float32, device=dev),
+            y=torch.empty(BUDGET, C, dtype=torch.bfloat16, device=dev),
+            o=torch.empty(T_all, HV, D, dtype=torch.bfloat16, device=dev)))
+    torch.cuda.synchronize()
+
+    # ---- launch lists: (kind, fn, args, bytes, flops) per engine step
+    i32 = np.dtype(np.int32).itemsize
+    plans = []
+    for si, st in enumerate(steps):
+        nd, npf = len(st.decodes), len(st.prefills)
+        tp = st.n_tokens - nd
+        off = int(offs[si])
+        calls = []
+        for ly in layers:
+            X, Y, O = ly["x"].data_ptr(), ly["y"].data_ptr(), ly["o"].data_ptr()
+            G, B = ly["g"].data_ptr(), ly["beta"].data_ptr()
+            yq, yk, yv = Y, Y + HK * D * 2, Y + 2 * HK * D * 2
+            if nd:
+                di = dec_idx_d.data_ptr() + int(dec_off[si]) * i32
+                calls.append(("conv_update", lib.gdn_causal_conv1d_update,
+                              (X + off * C * 2, C, ly["w"].data_ptr(), ly["b"].data_ptr(), ly["cs"].data_ptr(),
+                               SLOTS, di, Y, C, nd, C, K, 1, sptr),
+                              bytes_conv_update(nd), 0.0))
+            if npf:
+                qd = qsl_d.data_ptr() + int(qsl_off[si]) * i32
+                pi = pidx_d.data_ptr() + int(pidx_off[si]) * i32
+                ph = phi_d.data_ptr() + int(phi_off[si])
+                cd = ch_dev.data_ptr() + int(ch_off[si]) * 2 * i32
+                n_init = int(pf_hi[si].sum())
+                calls.append(("conv_varlen", lib.gdn_causal_conv1d_varlen,
+                              (X + (off + nd) * C * 2, C, ly["w"].data_ptr(), ly["b"].data_ptr(),
+                               ly["cs"].data_ptr(), SLOTS, qd, pi, ph, cd, n_chunks[si], Y + nd * C * 2, C,
+                               npf, tp, C, K, 1, sptr),
+                              bytes_conv_varlen(tp, npf, n_init, n_chunks[si]), 0.0))
+            if nd:
+                calls.append(("recurrent_decode", lib.gdn_fused_recurrent_decode,
+                              (yq, C, yk, C, yv, C, G + off * HV * 4, B + off * HV * 4, ly["state"].data_ptr(),
+                               SLOTS, None, di, None, O + off * HV * D * 2, HV * D, nd, nd, HK, HV, D, D,
+                               ctypes.c_float(1.0), 1, sptr),
+                              bytes_recurrent(nd, nd, nd), flops_recurrent(nd)))
+            if npf:
+                po = off + nd
+                calls.append(("recurrent_varlen", lib.gdn_fused_recurrent_decode,
+                              (yq + nd * C * 2, C, yk + nd * C * 2, C, yv + nd * C * 2, C, G + po * HV * 4,
+                               B + po * HV * 4, ly["state"].data_ptr(), SLOTS, qd, pi, ph,
+                               O + po * HV * D * 2, HV * D, npf, tp, HK, HV, D, D, ctypes.c_float(1.0), 1,
+                               sptr),
+                              bytes_recurrent(tp, n_init, npf), flops_recurrent(tp)))
+        plans.append(calls)
+
+    ch_host_ptr = ch_host.data_ptr()
+    n_out = ctypes.c_int32()
+
+    def run_pass(timing=None):
+        """One pass of the whole trace through every layer.  ``timing`` maps a
+        kernel kind to a list that receives (start, end) event pairs."""
+        for si, calls in enumerate(plans):
+            if n_chunks[si]:
+                # the step's chunk descriptors: built once on the host, uploaded once
+                a = int(ch_off[si])
+                rc = lib.gdn_build_conv_chunks(qsl_host[si].ctypes.data, len(pf_idx[si]),
+                                               ctypes.c_void_p(ch_host_ptr + a * 2 * i32), n_chunks[si],
+                                               ctypes.byref(n_out))
+                if rc != 0:
+                    raise RuntimeError("gdn_build_conv_chunks: " + lib.gdn_last_error().decode())
+                ch_dev[2 * a:2 * (a + n_chunks[si])].copy_(ch_host[2 * a:2 * (a + n_chunks[si])],
+                                                            non_blocking=True)
+            for kind, fn, fargs, _nb, _nf in calls:
+                rec = timing.get(kind) if timing is not None else None
+                if rec is not None:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                rc = fn(*fargs)
+                if rc != 0:
+                    raise RuntimeError("%s: %s" % (kind, lib.gdn_last_error().decode()))
+                if rec is not None:
+                    e1.record(stream)
+                    rec.append((e0, e1))
+
+    def totals(kind):
+        nb = sum(c[3] for calls in plans for c in calls if c[0] == kind)
+        nf = sum(c[4] for calls in plans for c in calls if c[0] == kind)
+        n = sum(1 for calls in plans for c in calls if c[0] == kind)
+        return n, nb, nf
+
+    kinds = ["conv_varlen", "conv_update", "recurrent_decode", "recurrent_varlen"]
+
+    # ---- warm-up, then one instrumented pass (untimed) for the per-kernel shares
+    for _ in range(args.warmup):
+        run_pass()
+    torch.cuda.synchronize()
+    prof = {k: [] for k in kinds}
+    run_pass(prof)
+    torch.cuda.synchronize()
+    kern = {}
+    for k in kinds:
+        ms = sum(e0.elapsed_time(e1) for e0, e1 in prof[k])
+        n, nb, nf = totals(k)
+        kern[k] = {"launches_per_step": n, "ms_per_step": ms, "avg_us": 1e3 * ms / max(n, 1),
+                   "gb_per_s": nb / (ms * 1e-3) / 1e9 if ms else 0.0,
+                   "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS if ms else 0.0}
+        if nf:
+            kern[k]["tflop_per_s"] = nf / (ms * 1e-3) / 1e12
+    dominant = max(kinds, key=lambda k: kern[k]["ms_per_step"])
+
+    # ---- timed region
+    torch.cuda.synchronize()
+    live = {dominant: []}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_pass(live)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_dom = sum(e0.elapsed_time(e1) for e0, e1 in live[dominant]) / args.steps
+    n, nb, nf = totals(dominant)
+    avg_us = 1e3 * ms_dom / n
+    if dominant == "recurrent_varlen":
+        achieved = nf / (ms_dom * 1e-3) / 1e12
+        roof = {"kernel": dominant, "bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
+                "avg_launch_us": avg_us, "algorithmic_per_launch": nf / n}
+    else:
+        achieved = nb / (ms_dom * 1e-3) / 1e9
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "avg_launch_us": avg_us, "algorithmic_per_launch": nb / n}
+
+    ms_per_step = 1e3 * wall / args.steps
+    value = T_all * L * args.steps / wall
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32", "io_dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "c32 engine-step trace: 128 requests x (1024 prompt + 128 output tokens), "
+                               "concurrency 32, 2048-token chunked-prefill budget, %d engine steps, "
+                               "%d tokens per layer, %d GDN layers" % (len(steps), T_all, L),
+                   "engine_steps": len(steps), "tokens_per_layer": T_all, "gdn_layers": L,
+                   "conv_channels": C, "conv_width": K, "qk_heads": HK, "v_heads": HV, "head_dim": D,
+                   "state_slots": SLOTS, "value_is": "tokens x layers / wall seconds"},
+        "roofline": roof,
+        "kernels": kern,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_sample_requests, trace.seq_len)
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

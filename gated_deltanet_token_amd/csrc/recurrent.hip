@@ -54,7 +54,9 @@ struct TokenIn {
     uint2 q[M];
 };
 
-template <int DK, int W, int R>
+// VARLEN only names the instantiation (decode and varlen launches show up as
+// separate kernels in a profile); the code is the same.
+template <int DK, int W, int R, bool VARLEN>
 __global__ __launch_bounds__(64 * W) void recurrent_kernel(RecurrentArgs a, int n_rowblocks) {
     using L = RowLayout<DK>;
     using Sh = RecurrentShape<DK, W, R>;
@@ -200,14 +202,14 @@ __global__ __launch_bounds__(64 * W) void recurrent_kernel(RecurrentArgs a, int 
     }
 }
 
-template <int DK, int W, int R>
+template <int DK, int W, int R, bool VARLEN>
 static hipError_t launch_shape(const RecurrentArgs &a, hipStream_t stream) {
     using Sh = RecurrentShape<DK, W, R>;
     const int nrb = (a.dv + Sh::kRowsPerBlock - 1) / Sh::kRowsPerBlock;
     const long long blocks = (long long)a.num_seqs * a.num_v_heads * nrb;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((recurrent_kernel<DK, W, R>), dim3((unsigned)blocks), dim3(Sh::kThreads), 0,
+    hipLaunchKernelGGL((recurrent_kernel<DK, W, R, VARLEN>), dim3((unsigned)blocks), dim3(Sh::kThreads), 0,
                        stream, a, nrb);
     return hipGetLastError();
 }
@@ -216,8 +218,8 @@ template <int DK>
 static hipError_t launch_dk(const RecurrentArgs &a, hipStream_t stream) {
     // decode (one token per sequence): 4 waves x 8 rows per workgroup;
     // varlen: the same shape for now.  Per-row arithmetic is shape-independent.
-    if (a.qsl == nullptr) return launch_shape<DK, 4, 1>(a, stream);
-    return launch_shape<DK, 4, 1>(a, stream);
+    if (a.qsl == nullptr) return launch_shape<DK, 4, 1, false>(a, stream);
+    return launch_shape<DK, 4, 1, true>(a, stream);
 }
 
 hipError_t launch_recurrent(const RecurrentArgs &a, hipStream_t stream) {
