@@ -1,7 +1,7 @@
 """Python binding of libgdn, the MI355X (gfx950) GDN token-mixer library.
 
 Argument marshalling only: every step of the path runs in the HIP kernels of
-``libgdn.so`` (built in-tree by ``gated_deltanet_token_amd.build``), reached
+``libgdn.so`` (built in-tree by ``gated_deltanet_token_amd/build.py``), reached
 through its C ABI (``include/gdn.h``).  PyTorch supplies device memory and
 streams.  There is no fallback: importing this package without the built
 library raises ``ImportError``.
@@ -26,7 +26,7 @@ CONV_WIDTH = 4
 
 # every entry point declared in include/gdn.h
 EXPORTS = ("gdn_last_error", "gdn_build_conv_chunks", "gdn_causal_conv1d_varlen",
-           "gdn_causal_conv1d_update", "gdn_fused_recurrent_decode")
+           "gdn_causal_conv1d_update", "gdn_fused_recurrent_decode", "gdn_chunk_gated_delta_rule")
 
 
 class GDNError(RuntimeError):
@@ -46,6 +46,7 @@ def _bind(path):
     lib.gdn_causal_conv1d_update.argtypes = [P, i64, P, P, P, i32, P, P, i64, i32, i32, i32, i32, P]
     lib.gdn_fused_recurrent_decode.argtypes = [P, i64, P, i64, P, i64, P, P, P, i32, P, P, P, P, i64,
                                                i32, i32, i32, i32, i32, i32, f32, i32, P]
+    lib.gdn_chunk_gated_delta_rule.argtypes = lib.gdn_fused_recurrent_decode.argtypes
     for name in EXPORTS[1:]:
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -60,7 +61,7 @@ def _hip_runtimes():
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libgdn.so is not built (%s); run python -m gated_deltanet_token_amd.build"
+    raise ImportError("libgdn.so is not built (%s); run python gated_deltanet_token_amd/build.py"
                       % LIB_PATH)
 # torch's HIP runtime must be the process's only one: load it first so that
 # libgdn's libamdhip64.so.7 dependency resolves to it (by soname)
@@ -174,15 +175,8 @@ def gdn_causal_conv1d_update(x, weight, bias, conv_state, state_indices, y, silu
     _check(rc, "gdn_causal_conv1d_update")
 
 
-def gdn_fused_recurrent_decode(q, k, v, g, beta, state, state_indices, o, query_start_loc=None,
-                               has_initial_state=None, scale=1.0, qk_l2norm=True, stream=None):
-    """Gated delta rule over packed tokens; see gdn.h.
-
-    q, k: bf16 [T][HK][dk]; v: bf16 [T][HV][dv] (token rows may be strided
-    views of one wider activation); g, beta: fp32 [T][HV]; state: fp32
-    [slots][HV][dv][dk] (in place); o: bf16 [T][HV][dv]; query_start_loc
-    int32 [S+1] or None (one token per sequence, S = T).
-    """
+def _recurrent(func, q, k, v, g, beta, state, state_indices, o, query_start_loc, has_initial_state, scale,
+               qk_l2norm, stream):
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
         _dtype(t, torch.bfloat16, n)
@@ -196,9 +190,30 @@ def gdn_fused_recurrent_decode(q, k, v, g, beta, state, state_indices, o, query_
     T, HK, dk = q.shape
     HV, dv = v.shape[1], v.shape[2]
     S = state_indices.numel()
-    rc = lib.gdn_fused_recurrent_decode(
+    rc = getattr(lib, func)(
         _ptr(q), _heads(q, "q"), _ptr(k), _heads(k, "k"), _ptr(v), _heads(v, "v"), _ptr(g),
         _ptr(beta), _ptr(state), state.shape[0], _ptr(query_start_loc), _ptr(state_indices),
         _ptr(has_initial_state), _ptr(o), _heads(o, "o"), S, T, HK, HV, dk, dv, float(scale),
         int(bool(qk_l2norm)), _stream(stream))
-    _check(rc, "gdn_fused_recurrent_decode")
+    _check(rc, func)
+
+
+def gdn_fused_recurrent_decode(q, k, v, g, beta, state, state_indices, o, query_start_loc=None,
+                               has_initial_state=None, scale=1.0, qk_l2norm=True, stream=None):
+    """Gated delta rule over packed tokens, token by token; see gdn.h.
+
+    q, k: bf16 [T][HK][dk]; v: bf16 [T][HV][dv] (token rows may be strided
+    views of one wider activation); g, beta: fp32 [T][HV]; state: fp32
+    [slots][HV][dv][dk] (in place); o: bf16 [T][HV][dv]; query_start_loc
+    int32 [S+1] or None (one token per sequence, S = T).
+    """
+    _recurrent("gdn_fused_recurrent_decode", q, k, v, g, beta, state, state_indices, o, query_start_loc,
+               has_initial_state, scale, qk_l2norm, stream)
+
+
+def gdn_chunk_gated_delta_rule(q, k, v, g, beta, state, state_indices, o, query_start_loc,
+                               has_initial_state=None, scale=1.0, qk_l2norm=True, stream=None):
+    """The same rule over packed prefill tokens, chunkwise on the matrix
+    cores (dk = 128, dv a multiple of 32); see gdn.h."""
+    _recurrent("gdn_chunk_gated_delta_rule", q, k, v, g, beta, state, state_indices, o, query_start_loc,
+               has_initial_state, scale, qk_l2norm, stream)

@@ -1,6 +1,7 @@
 """Build libgdn.so in-tree for gfx950 with hipcc.
 
-Usage: python -m gated_deltanet_token_amd.build   (or __graft_entry__.build())
+Usage: python gated_deltanet_token_amd/build.py   (or __graft_entry__.build());
+this script never imports the package, which binds the library on import.
 
 Every .hip source under csrc/ is compiled to an object in _build/ and linked
 into gated_deltanet_token_amd/libgdn.so.  Packed-FP32 instruction selection

@@ -125,13 +125,16 @@ GDN_EXPORT int gdn_causal_conv1d_update(const gdn_bf16 *x, int64_t x_stride, con
     return hip_status(gdn::launch_conv_update(a, (hipStream_t)stream), "conv update launch");
 }
 
-GDN_EXPORT int gdn_fused_recurrent_decode(const gdn_bf16 *q, int64_t q_stride, const gdn_bf16 *k, int64_t k_stride,
-                                          const gdn_bf16 *v, int64_t v_stride, const float *g, const float *beta,
-                                          float *state, int32_t num_slots, const int32_t *query_start_loc,
-                                          const int32_t *state_indices, const uint8_t *has_initial_state,
-                                          gdn_bf16 *o, int64_t o_stride, int32_t num_seqs, int32_t num_tokens,
-                                          int32_t num_k_heads, int32_t num_v_heads, int32_t head_k_dim,
-                                          int32_t head_v_dim, float scale, int32_t qk_l2norm, void *stream) {
+namespace {
+
+// shared validation of the two recurrence entry points; returns GDN_OK and
+// fills `a` when the call is valid and non-empty, 1 when there is nothing to do
+int check_recurrent(const gdn_bf16 *q, int64_t q_stride, const gdn_bf16 *k, int64_t k_stride, const gdn_bf16 *v,
+                    int64_t v_stride, const float *g, const float *beta, float *state, int32_t num_slots,
+                    const int32_t *query_start_loc, const int32_t *state_indices, const uint8_t *has_initial_state,
+                    gdn_bf16 *o, int64_t o_stride, int32_t num_seqs, int32_t num_tokens, int32_t num_k_heads,
+                    int32_t num_v_heads, int32_t head_k_dim, int32_t head_v_dim, float scale, int32_t qk_l2norm,
+                    gdn::RecurrentArgs &a) {
     if (!q || !k || !v || !g || !beta || !state || !state_indices || !o)
         return fail(GDN_ERR_INVALID, "q, k, v, g, beta, state, state_indices and o are required");
     if (num_seqs < 0 || num_tokens < 0) return fail(GDN_ERR_INVALID, "negative num_seqs or num_tokens");
@@ -156,9 +159,49 @@ GDN_EXPORT int gdn_fused_recurrent_decode(const gdn_bf16 *q, int64_t q_stride, c
         overlap(os, row_span(k, num_tokens, k_stride, qk_w, 2)) ||
         overlap(os, row_span(v, num_tokens, v_stride, v_w, 2)))
         return fail(GDN_ERR_INVALID, "o overlaps q, k or v");
-    if (num_seqs == 0 || num_tokens == 0) return ok();
-    gdn::RecurrentArgs a{q, q_stride, k, k_stride, v, v_stride, g, beta, state, query_start_loc, state_indices,
-                         has_initial_state, o, o_stride, num_seqs, num_k_heads, num_v_heads, head_k_dim,
-                         head_v_dim, scale, qk_l2norm};
+    if (num_seqs == 0 || num_tokens == 0) {
+        ok();
+        return 1;
+    }
+    a = gdn::RecurrentArgs{q, q_stride, k, k_stride, v, v_stride, g, beta, state, query_start_loc, state_indices,
+                           has_initial_state, o, o_stride, num_seqs, num_k_heads, num_v_heads, head_k_dim,
+                           head_v_dim, scale, qk_l2norm};
+    return GDN_OK;
+}
+
+}  // namespace
+
+GDN_EXPORT int gdn_fused_recurrent_decode(const gdn_bf16 *q, int64_t q_stride, const gdn_bf16 *k, int64_t k_stride,
+                                          const gdn_bf16 *v, int64_t v_stride, const float *g, const float *beta,
+                                          float *state, int32_t num_slots, const int32_t *query_start_loc,
+                                          const int32_t *state_indices, const uint8_t *has_initial_state,
+                                          gdn_bf16 *o, int64_t o_stride, int32_t num_seqs, int32_t num_tokens,
+                                          int32_t num_k_heads, int32_t num_v_heads, int32_t head_k_dim,
+                                          int32_t head_v_dim, float scale, int32_t qk_l2norm, void *stream) {
+    gdn::RecurrentArgs a;
+    const int rc = check_recurrent(q, q_stride, k, k_stride, v, v_stride, g, beta, state, num_slots,
+                                   query_start_loc, state_indices, has_initial_state, o, o_stride, num_seqs,
+                                   num_tokens, num_k_heads, num_v_heads, head_k_dim, head_v_dim, scale, qk_l2norm, a);
+    if (rc == 1) return GDN_OK;
+    if (rc) return rc;
     return hip_status(gdn::launch_recurrent(a, (hipStream_t)stream), "recurrent launch");
+}
+
+GDN_EXPORT int gdn_chunk_gated_delta_rule(const gdn_bf16 *q, int64_t q_stride, const gdn_bf16 *k, int64_t k_stride,
+                                          const gdn_bf16 *v, int64_t v_stride, const float *g, const float *beta,
+                                          float *state, int32_t num_slots, const int32_t *query_start_loc,
+                                          const int32_t *state_indices, const uint8_t *has_initial_state,
+                                          gdn_bf16 *o, int64_t o_stride, int32_t num_seqs, int32_t num_tokens,
+                                          int32_t num_k_heads, int32_t num_v_heads, int32_t head_k_dim,
+                                          int32_t head_v_dim, float scale, int32_t qk_l2norm, void *stream) {
+    if (!query_start_loc) return fail(GDN_ERR_INVALID, "query_start_loc is required");
+    gdn::RecurrentArgs a;
+    const int rc = check_recurrent(q, q_stride, k, k_stride, v, v_stride, g, beta, state, num_slots,
+                                   query_start_loc, state_indices, has_initial_state, o, o_stride, num_seqs,
+                                   num_tokens, num_k_heads, num_v_heads, head_k_dim, head_v_dim, scale, qk_l2norm, a);
+    if (rc == 1) return GDN_OK;
+    if (rc) return rc;
+    if (head_k_dim != 128) return fail(GDN_ERR_UNSUPPORTED, "chunked form: head_k_dim must be 128");
+    if (head_v_dim % 32) return fail(GDN_ERR_UNSUPPORTED, "chunked form: head_v_dim must be a multiple of 32");
+    return hip_status(gdn::launch_chunk_recurrent(a, (hipStream_t)stream), "chunk recurrent launch");
 }

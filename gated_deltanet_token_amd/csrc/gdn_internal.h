@@ -67,5 +67,6 @@ struct RecurrentArgs {
 hipError_t launch_conv_varlen(const ConvVarlenArgs &a, hipStream_t stream);
 hipError_t launch_conv_update(const ConvUpdateArgs &a, hipStream_t stream);
 hipError_t launch_recurrent(const RecurrentArgs &a, hipStream_t stream);
+hipError_t launch_chunk_recurrent(const RecurrentArgs &a, hipStream_t stream);
 
 }  // namespace gdn

@@ -2,12 +2,14 @@
  * gdn.h -- C ABI of the Gated DeltaNet (GDN) token-mixer library for AMD
  * Instinct MI355X (gfx950).
  *
- * Four calls form the layer's data-parallel hot path:
+ * The calls that form the layer's data-parallel hot path:
  *
  *   gdn_build_conv_chunks       host: exact (sequence, 8-token chunk) list
  *   gdn_causal_conv1d_varlen    GPU: width-4 causal conv over packed prefill
  *   gdn_causal_conv1d_update    GPU: single-token conv for decode
  *   gdn_fused_recurrent_decode  GPU: gated delta rule over packed tokens
+ *   gdn_chunk_gated_delta_rule  GPU: the same rule over prefill tokens,
+ *                               chunkwise on the matrix cores
  *
  * Conventions shared by every call
  * --------------------------------
@@ -200,6 +202,43 @@ int gdn_causal_conv1d_update(const gdn_bf16 *x, int64_t x_stride,
  * of 8 up to 256, alignment contract); GDN_ERR_HIP.
  */
 int gdn_fused_recurrent_decode(const gdn_bf16 *q, int64_t q_stride,
+                               const gdn_bf16 *k, int64_t k_stride,
+                               const gdn_bf16 *v, int64_t v_stride,
+                               const float *g, const float *beta,
+                               float *state, int32_t num_slots,
+                               const int32_t *query_start_loc,
+                               const int32_t *state_indices,
+                               const uint8_t *has_initial_state,
+                               gdn_bf16 *o, int64_t o_stride,
+                               int32_t num_seqs, int32_t num_tokens,
+                               int32_t num_k_heads, int32_t num_v_heads,
+                               int32_t head_k_dim, int32_t head_v_dim,
+                               float scale, int32_t qk_l2norm, void *stream);
+
+/*
+ * gdn_chunk_gated_delta_rule -- the same gated delta rule as
+ * gdn_fused_recurrent_decode over packed prefill tokens, evaluated chunk by
+ * chunk (64 tokens) in the equivalent matrix form on the matrix cores.
+ *
+ * Sources: the rule from Yang, Kautz, Hatamizadeh, "Gated Delta Networks:
+ * Improving Mamba2 with Delta Rule" (ICLR 2025); its chunkwise form follows
+ * from unrolling the recurrence over a chunk: with u_t the per-token update
+ * vector, (I + A) U = R for a unit lower-triangular A built from the chunk's
+ * keys, gates and betas (the pages name the prefill GDN path only by its
+ * test, page "Qwen3.5-4b BF16 optimization and correctness (sm_120)",
+ * section "Evidence").
+ *
+ * Arguments, layouts, state semantics and errors are those of
+ * gdn_fused_recurrent_decode, except:
+ *   query_start_loc  required (int32 [num_seqs + 1])
+ *   head_k_dim       must be 128
+ *   head_v_dim       a positive multiple of 32 up to 256
+ * Results equal the per-token recurrence up to fp32 rounding (a different
+ * association of the same sums); sequence lengths need not be multiples of
+ * 64.  Splitting a sequence across calls moves the chunk boundaries, so it
+ * changes results only within that rounding.
+ */
+int gdn_chunk_gated_delta_rule(const gdn_bf16 *q, int64_t q_stride,
                                const gdn_bf16 *k, int64_t k_stride,
                                const gdn_bf16 *v, int64_t v_stride,
                                const float *g, const float *beta,

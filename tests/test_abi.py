@@ -149,3 +149,21 @@ def test_error_text_cleared_on_success():
     assert gdn.lib.gdn_last_error()
     gdn.gdn_build_conv_chunks([0, 4])
     assert gdn.lib.gdn_last_error() == b""
+
+
+def chunk(**kw):
+    a = dict(q=Q, qs=2048, k=K_, ks=2048, v=V, vs=4096, g=G, b=BE, st=ST, slots=64, qsl=QSL, idx=IDX,
+             hi=None, o=O, os=4096, S=3, T=2019, HK=16, HV=32, dk=128, dv=128, scale=1.0, norm=1)
+    a.update(kw)
+    return gdn.lib.gdn_chunk_gated_delta_rule(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["g"],
+                                              a["b"], a["st"], a["slots"], a["qsl"], a["idx"], a["hi"],
+                                              a["o"], a["os"], a["S"], a["T"], a["HK"], a["HV"], a["dk"],
+                                              a["dv"], a["scale"], a["norm"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qsl=None), INV), (dict(q=None), INV), (dict(HV=24), INV), (dict(o=V), INV),
+    (dict(dk=64), UNS), (dict(dk=16), UNS), (dict(dv=48), UNS), (dict(dv=512), UNS), (dict(q=Q + 8), UNS),
+])
+def test_chunk_validation(kw, code):
+    assert chunk(**kw) == code, gdn.lib.gdn_last_error()
