@@ -12,8 +12,9 @@ in the 256 MB Infinity Cache, as in a model with several GDN layers.
 Per engine step: the host builds the exact (sequence, 8-token chunk)
 descriptors once (gdn_build_conv_chunks) and uploads them once; then for every
 layer: conv update for the decode rows, varlen conv for the prefill rows,
-the fused recurrence for the decodes and for the prefill chunks (q, k, v
-are column views of the conv output).  Inputs are resident in HBM before the
+the fused recurrence for the decodes and the chunkwise (matrix-core) form of
+the same rule for the prefill chunks (q, k, v are column views of the conv
+output).  Inputs are resident in HBM before the
 timed region; every call goes through the C ABI on torch's current stream.
 
 Output: one JSON line.  ``value`` is GDN-layer tokens per second (tokens x
@@ -38,7 +39,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GDN layer tokens/s + achieved HBM GB/s (% peak), c32 prefill & decode"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 C, HK, HV, D, K = 8192, 16, 32, 128, 4
 SLOTS = 64
@@ -191,6 +192,12 @@ def main():
             o=torch.empty(T_all, HV, D, dtype=torch.bfloat16, device=dev)))
     torch.cuda.synchronize()
 
+    # scratch of the chunkwise recurrence, sized for the largest prefill step
+    # and shared by every call (they are ordered on one stream)
+    ws_bytes = max(gdn.gdn_chunk_workspace_size(len(pf_idx[i]), steps[i].n_tokens - len(steps[i].decodes), HK, HV)
+                   for i in range(len(steps)))
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
     # ---- launch lists: (kind, fn, args, bytes, flops) per engine step
     i32 = np.dtype(np.int32).itemsize
     plans = []
@@ -228,11 +235,11 @@ def main():
                               bytes_recurrent(nd, nd, nd), flops_recurrent(nd)))
             if npf:
                 po = off + nd
-                calls.append(("recurrent_varlen", lib.gdn_fused_recurrent_decode,
+                calls.append(("recurrent_chunk", lib.gdn_chunk_gated_delta_rule,
                               (yq + nd * C * 2, C, yk + nd * C * 2, C, yv + nd * C * 2, C, G + po * HV * 4,
                                B + po * HV * 4, ly["state"].data_ptr(), SLOTS, qd, pi, ph,
-                               O + po * HV * D * 2, HV * D, npf, tp, HK, HV, D, D, ctypes.c_float(1.0), 1,
-                               sptr),
+                               O + po * HV * D * 2, HV * D, npf, tp, HK, HV, D, D, ws.data_ptr(), ws_bytes,
+                               ctypes.c_float(1.0), 1, sptr),
                               bytes_recurrent(tp, n_init, npf), flops_recurrent(tp)))
         plans.append(calls)
 
@@ -272,7 +279,7 @@ def main():
         n = sum(1 for calls in plans for c in calls if c[0] == kind)
         return n, nb, nf
 
-    kinds = ["conv_varlen", "conv_update", "recurrent_decode", "recurrent_varlen"]
+    kinds = ["conv_varlen", "conv_update", "recurrent_decode", "recurrent_chunk"]
 
     # ---- warm-up, then one instrumented pass (untimed) for the per-kernel shares
     for _ in range(args.warmup):
@@ -304,10 +311,12 @@ def main():
     ms_dom = sum(e0.elapsed_time(e1) for e0, e1 in live[dominant]) / args.steps
     n, nb, nf = totals(dominant)
     avg_us = 1e3 * ms_dom / n
-    if dominant == "recurrent_varlen":
+    if dominant == "recurrent_chunk":
+        # matrix-core kernel (bf16 MFMA, fp32 operands split hi+lo); algorithmic
+        # flops of the rule against the dense bf16 MFMA peak
         achieved = nf / (ms_dom * 1e-3) / 1e12
-        roof = {"kernel": dominant, "bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
                 "avg_launch_us": avg_us, "algorithmic_per_launch": nf / n}
     else:
         achieved = nb / (ms_dom * 1e-3) / 1e9

@@ -26,7 +26,8 @@ CONV_WIDTH = 4
 
 # every entry point declared in include/gdn.h
 EXPORTS = ("gdn_last_error", "gdn_build_conv_chunks", "gdn_causal_conv1d_varlen",
-           "gdn_causal_conv1d_update", "gdn_fused_recurrent_decode", "gdn_chunk_gated_delta_rule")
+           "gdn_causal_conv1d_update", "gdn_fused_recurrent_decode", "gdn_chunk_gated_delta_rule",
+           "gdn_chunk_workspace_size")
 
 
 class GDNError(RuntimeError):
@@ -46,9 +47,12 @@ def _bind(path):
     lib.gdn_causal_conv1d_update.argtypes = [P, i64, P, P, P, i32, P, P, i64, i32, i32, i32, i32, P]
     lib.gdn_fused_recurrent_decode.argtypes = [P, i64, P, i64, P, i64, P, P, P, i32, P, P, P, P, i64,
                                                i32, i32, i32, i32, i32, i32, f32, i32, P]
-    lib.gdn_chunk_gated_delta_rule.argtypes = lib.gdn_fused_recurrent_decode.argtypes
-    for name in EXPORTS[1:]:
+    lib.gdn_chunk_gated_delta_rule.argtypes = [P, i64, P, i64, P, i64, P, P, P, i32, P, P, P, P, i64,
+                                               i32, i32, i32, i32, i32, i32, P, ctypes.c_size_t, f32, i32, P]
+    for name in EXPORTS[1:-1]:
         getattr(lib, name).restype = ctypes.c_int
+    lib.gdn_chunk_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.gdn_chunk_workspace_size.restype = ctypes.c_size_t
     return lib
 
 
@@ -176,7 +180,7 @@ def gdn_causal_conv1d_update(x, weight, bias, conv_state, state_indices, y, silu
 
 
 def _recurrent(func, q, k, v, g, beta, state, state_indices, o, query_start_loc, has_initial_state, scale,
-               qk_l2norm, stream):
+               qk_l2norm, stream, workspace=None):
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
         _dtype(t, torch.bfloat16, n)
@@ -190,12 +194,16 @@ def _recurrent(func, q, k, v, g, beta, state, state_indices, o, query_start_loc,
     T, HK, dk = q.shape
     HV, dv = v.shape[1], v.shape[2]
     S = state_indices.numel()
-    rc = getattr(lib, func)(
-        _ptr(q), _heads(q, "q"), _ptr(k), _heads(k, "k"), _ptr(v), _heads(v, "v"), _ptr(g),
-        _ptr(beta), _ptr(state), state.shape[0], _ptr(query_start_loc), _ptr(state_indices),
-        _ptr(has_initial_state), _ptr(o), _heads(o, "o"), S, T, HK, HV, dk, dv, float(scale),
-        int(bool(qk_l2norm)), _stream(stream))
-    _check(rc, func)
+    args = [_ptr(q), _heads(q, "q"), _ptr(k), _heads(k, "k"), _ptr(v), _heads(v, "v"), _ptr(g),
+            _ptr(beta), _ptr(state), state.shape[0], _ptr(query_start_loc), _ptr(state_indices),
+            _ptr(has_initial_state), _ptr(o), _heads(o, "o"), S, T, HK, HV, dk, dv]
+    if func == "gdn_chunk_gated_delta_rule":
+        need = gdn_chunk_workspace_size(S, T, HK, HV)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        args += [_ptr(workspace), workspace.numel() * workspace.element_size()]
+    args += [float(scale), int(bool(qk_l2norm)), _stream(stream)]
+    _check(getattr(lib, func)(*args), func)
 
 
 def gdn_fused_recurrent_decode(q, k, v, g, beta, state, state_indices, o, query_start_loc=None,
@@ -211,9 +219,17 @@ def gdn_fused_recurrent_decode(q, k, v, g, beta, state, state_indices, o, query_
                has_initial_state, scale, qk_l2norm, stream)
 
 
+def gdn_chunk_workspace_size(num_seqs, num_tokens, num_k_heads, num_v_heads) -> int:
+    """Bytes of device scratch gdn_chunk_gated_delta_rule needs."""
+    return int(lib.gdn_chunk_workspace_size(num_seqs, num_tokens, num_k_heads, num_v_heads))
+
+
 def gdn_chunk_gated_delta_rule(q, k, v, g, beta, state, state_indices, o, query_start_loc,
-                               has_initial_state=None, scale=1.0, qk_l2norm=True, stream=None):
+                               has_initial_state=None, scale=1.0, qk_l2norm=True, stream=None,
+                               workspace=None):
     """The same rule over packed prefill tokens, chunkwise on the matrix
-    cores (dk = 128, dv a multiple of 32); see gdn.h."""
+    cores (dk = 128, dv a multiple of 32); see gdn.h.  ``workspace`` is a
+    device byte tensor of at least gdn_chunk_workspace_size(...) bytes; when
+    omitted, torch allocates one for the call."""
     _recurrent("gdn_chunk_gated_delta_rule", q, k, v, g, beta, state, state_indices, o, query_start_loc,
-               has_initial_state, scale, qk_l2norm, stream)
+               has_initial_state, scale, qk_l2norm, stream, workspace)

@@ -187,13 +187,20 @@ GDN_EXPORT int gdn_fused_recurrent_decode(const gdn_bf16 *q, int64_t q_stride, c
     return hip_status(gdn::launch_recurrent(a, (hipStream_t)stream), "recurrent launch");
 }
 
+GDN_EXPORT size_t gdn_chunk_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_k_heads,
+                                           int32_t num_v_heads) {
+    if (num_seqs < 0 || num_tokens < 0 || num_k_heads < 0 || num_v_heads < 0) return 0;
+    return (size_t)gdn::chunk_workspace_bytes(num_seqs, num_tokens, num_k_heads, num_v_heads);
+}
+
 GDN_EXPORT int gdn_chunk_gated_delta_rule(const gdn_bf16 *q, int64_t q_stride, const gdn_bf16 *k, int64_t k_stride,
                                           const gdn_bf16 *v, int64_t v_stride, const float *g, const float *beta,
                                           float *state, int32_t num_slots, const int32_t *query_start_loc,
                                           const int32_t *state_indices, const uint8_t *has_initial_state,
                                           gdn_bf16 *o, int64_t o_stride, int32_t num_seqs, int32_t num_tokens,
                                           int32_t num_k_heads, int32_t num_v_heads, int32_t head_k_dim,
-                                          int32_t head_v_dim, float scale, int32_t qk_l2norm, void *stream) {
+                                          int32_t head_v_dim, void *workspace, size_t workspace_bytes,
+                                          float scale, int32_t qk_l2norm, void *stream) {
     if (!query_start_loc) return fail(GDN_ERR_INVALID, "query_start_loc is required");
     gdn::RecurrentArgs a;
     const int rc = check_recurrent(q, q_stride, k, k_stride, v, v_stride, g, beta, state, num_slots,
@@ -203,5 +210,11 @@ GDN_EXPORT int gdn_chunk_gated_delta_rule(const gdn_bf16 *q, int64_t q_stride, c
     if (rc) return rc;
     if (head_k_dim != 128) return fail(GDN_ERR_UNSUPPORTED, "chunked form: head_k_dim must be 128");
     if (head_v_dim % 32) return fail(GDN_ERR_UNSUPPORTED, "chunked form: head_v_dim must be a multiple of 32");
-    return hip_status(gdn::launch_chunk_recurrent(a, (hipStream_t)stream), "chunk recurrent launch");
+    const size_t need = (size_t)gdn::chunk_workspace_bytes(num_seqs, num_tokens, num_k_heads, num_v_heads);
+    if (!workspace) return fail(GDN_ERR_INVALID, "workspace is required (%zu bytes)", need);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(GDN_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(GDN_ERR_CAPACITY, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    return hip_status(gdn::launch_chunk_recurrent(a, workspace, num_tokens, (hipStream_t)stream),
+                      "chunk recurrent launch");
 }

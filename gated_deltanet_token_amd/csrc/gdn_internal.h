@@ -67,6 +67,8 @@ struct RecurrentArgs {
 hipError_t launch_conv_varlen(const ConvVarlenArgs &a, hipStream_t stream);
 hipError_t launch_conv_update(const ConvUpdateArgs &a, hipStream_t stream);
 hipError_t launch_recurrent(const RecurrentArgs &a, hipStream_t stream);
-hipError_t launch_chunk_recurrent(const RecurrentArgs &a, hipStream_t stream);
+// chunkwise form: workspace of chunk_workspace_bytes(...) bytes, 256-byte aligned
+int64_t chunk_workspace_bytes(int num_seqs, int num_tokens, int num_k_heads, int num_v_heads);
+hipError_t launch_chunk_recurrent(const RecurrentArgs &a, void *workspace, int num_tokens, hipStream_t stream);
 
 }  // namespace gdn

@@ -10,15 +10,17 @@
  *   gdn_fused_recurrent_decode  GPU: gated delta rule over packed tokens
  *   gdn_chunk_gated_delta_rule  GPU: the same rule over prefill tokens,
  *                               chunkwise on the matrix cores
+ *   gdn_chunk_workspace_size    host: scratch bytes the chunkwise call needs
  *
  * Conventions shared by every call
  * --------------------------------
  * - bf16 values travel as raw 16-bit patterns (gdn_bf16).  fp32 -> bf16
  *   rounding is round-to-nearest-even.  Arithmetic is fp32.
  * - Unless marked "host", a pointer is a device pointer (HBM of the current
- *   HIP device).  The caller owns every buffer.  The library never allocates,
- *   frees or caches device memory or pointers, holds no global mutable state
- *   and may be called from several threads (each on its own buffers).
+ *   HIP device).  The caller owns every buffer, scratch workspaces included.
+ *   The library never allocates, frees or caches device memory or pointers,
+ *   holds no global mutable state and may be called from several threads
+ *   (each on its own buffers).
  * - GPU calls validate their arguments on the host, then enqueue kernels on
  *   `stream` (a hipStream_t; NULL = the default stream) and return without
  *   waiting.  A call that returns an error enqueued nothing.
@@ -39,6 +41,7 @@
 #ifndef GDN_H
 #define GDN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -62,7 +65,7 @@ typedef enum gdn_status {
     GDN_OK = 0,
     GDN_ERR_INVALID = -1,      /* NULL pointer, bad count, bad pair, aliasing */
     GDN_ERR_UNSUPPORTED = -2,  /* width != 4, misaligned, unsupported head dim */
-    GDN_ERR_CAPACITY = -3,     /* descriptor buffer too small */
+    GDN_ERR_CAPACITY = -3,     /* descriptor buffer or workspace too small */
     GDN_ERR_HIP = -4           /* the HIP runtime reported an error */
 } gdn_status;
 
@@ -228,16 +231,31 @@ int gdn_fused_recurrent_decode(const gdn_bf16 *q, int64_t q_stride,
  * test, page "Qwen3.5-4b BF16 optimization and correctness (sm_120)",
  * section "Evidence").
  *
+ * Two kernels run on `stream`: one prepares, for every (64-token chunk,
+ * v-head) in parallel, the parts that do not depend on the state (the
+ * inverse of I + A, the masked decayed Q K^T, per-token factors, K^T) in
+ * `workspace`; the second walks each sequence's chunks in order.
+ *
  * Arguments, layouts, state semantics and errors are those of
  * gdn_fused_recurrent_decode, except:
  *   query_start_loc  required (int32 [num_seqs + 1])
  *   head_k_dim       must be 128
  *   head_v_dim       a positive multiple of 32 up to 256
+ *   workspace        device scratch owned by the caller, 256-byte aligned,
+ *                    at least gdn_chunk_workspace_size(num_seqs, num_tokens,
+ *                    num_k_heads, num_v_heads) bytes; its contents on entry
+ *                    do not matter and are overwritten.  Calls that share a
+ *                    workspace must not overlap in time.
+ * Errors beyond those: GDN_ERR_INVALID (NULL workspace), GDN_ERR_UNSUPPORTED
+ * (misaligned workspace), GDN_ERR_CAPACITY (workspace_bytes too small).
  * Results equal the per-token recurrence up to fp32 rounding (a different
  * association of the same sums); sequence lengths need not be multiples of
  * 64.  Splitting a sequence across calls moves the chunk boundaries, so it
  * changes results only within that rounding.
  */
+size_t gdn_chunk_workspace_size(int32_t num_seqs, int32_t num_tokens,
+                                int32_t num_k_heads, int32_t num_v_heads);
+
 int gdn_chunk_gated_delta_rule(const gdn_bf16 *q, int64_t q_stride,
                                const gdn_bf16 *k, int64_t k_stride,
                                const gdn_bf16 *v, int64_t v_stride,
@@ -250,6 +268,7 @@ int gdn_chunk_gated_delta_rule(const gdn_bf16 *q, int64_t q_stride,
                                int32_t num_seqs, int32_t num_tokens,
                                int32_t num_k_heads, int32_t num_v_heads,
                                int32_t head_k_dim, int32_t head_v_dim,
+                               void *workspace, size_t workspace_bytes,
                                float scale, int32_t qk_l2norm, void *stream);
 
 #ifdef __cplusplus

@@ -151,19 +151,34 @@ def test_error_text_cleared_on_success():
     assert gdn.lib.gdn_last_error() == b""
 
 
+WS = A + 0x40000000
+WS_NEED = gdn.gdn_chunk_workspace_size(3, 2019, 16, 32)
+
+
 def chunk(**kw):
     a = dict(q=Q, qs=2048, k=K_, ks=2048, v=V, vs=4096, g=G, b=BE, st=ST, slots=64, qsl=QSL, idx=IDX,
-             hi=None, o=O, os=4096, S=3, T=2019, HK=16, HV=32, dk=128, dv=128, scale=1.0, norm=1)
+             hi=None, o=O, os=4096, S=3, T=2019, HK=16, HV=32, dk=128, dv=128, ws=WS, wsb=WS_NEED,
+             scale=1.0, norm=1)
     a.update(kw)
     return gdn.lib.gdn_chunk_gated_delta_rule(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["g"],
                                               a["b"], a["st"], a["slots"], a["qsl"], a["idx"], a["hi"],
                                               a["o"], a["os"], a["S"], a["T"], a["HK"], a["HV"], a["dk"],
-                                              a["dv"], a["scale"], a["norm"], None)
+                                              a["dv"], a["ws"], a["wsb"], a["scale"], a["norm"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(qsl=None), INV), (dict(q=None), INV), (dict(HV=24), INV), (dict(o=V), INV),
     (dict(dk=64), UNS), (dict(dk=16), UNS), (dict(dv=48), UNS), (dict(dv=512), UNS), (dict(q=Q + 8), UNS),
+    (dict(ws=None), INV), (dict(ws=WS + 128), UNS), (dict(wsb=WS_NEED - 1), CAP),
 ])
 def test_chunk_validation(kw, code):
     assert chunk(**kw) == code, gdn.lib.gdn_last_error()
+
+
+def test_chunk_workspace_size_formula():
+    # per (64-token chunk, v-head): T and P as hi/lo bf16 (4 x 8 KiB) + 5 x 64
+    # fp32 factors; per (chunk, q/k head): K^T (16 KiB); chunks bounded by
+    # ceil(T / 64) + S
+    for S, T, HK, HV in ((3, 2019, 16, 32), (1, 1, 1, 1), (2, 2048, 16, 32), (0, 0, 16, 32)):
+        mc = (T + 63) // 64 + S
+        assert gdn.gdn_chunk_workspace_size(S, T, HK, HV) == mc * (HV * (4 * 8192 + 5 * 256) + HK * 16384)
