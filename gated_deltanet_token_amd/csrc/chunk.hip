@@ -18,8 +18,10 @@
 //    -- written to the caller's workspace;
 //  * scan (one workgroup per (sequence, v-head, 32 v rows), serial over the
 //    sequence's chunks): [K;Q] S0^T, R, U = T R, o = S0 part + P U and
-//    S_C = G_C S0 + U'^T K, with the state slice held in VGPRs in the MFMA
-//    accumulator layout and the next chunk's inputs prefetched.
+//    S_C^T = G_C S0^T + K^T U', with the state slice held transposed in VGPRs
+//    in the MFMA accumulator layout (so every lane holds 4 consecutive dims
+//    of a row and all LDS / global traffic is 8- or 16-byte vectors) and the
+//    next chunk's inputs prefetched.
 //
 // Precision: products of raw bf16 inputs (K K^T, Q K^T) are exact in the
 // bf16 MFMA with fp32 accumulation.  Every product with an fp32 operand (the
@@ -80,10 +82,25 @@ __device__ __forceinline__ f32x4 mma(const bf16x8 &a, const bf16x8 &b, const f32
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ void split(float v, __bf16 &hi, __bf16 &lo) {
     hi = (__bf16)v;
     lo = (__bf16)(v - (float)hi);
 }
+
+// four fp32 -> hi and lo bf16x4 (8-byte stores)
+__device__ __forceinline__ void split4(const f32x4 &v, bf16x4 &hi, bf16x4 &lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        __bf16 h, l;
+        split(v[e], h, l);
+        hi[e] = h;
+        lo[e] = l;
+    }
+}
+
+__device__ __forceinline__ void st4(__bf16 *p, const bf16x4 &v) { *reinterpret_cast<bf16x4 *>(p) = v; }
 
 // C += X Y for 16x16 fp32 tiles in LDS; four 16x16x4 fp32 MFMAs
 __device__ __forceinline__ f32x4 mm16_f32(const float (*X)[LDF], int xr, int xc, const float (*Y)[LDF], int yr,
@@ -163,8 +180,6 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
             for (int m = 0; m < 4; ++m) kv[m] = qv[m] = make_uint4(0, 0, 0, 0);
         }
         float skk = 0.f, sqq = 0.f;
-        const bool write_kt = (h % grp) == 0;
-        __bf16 *ktg = &kts[(int64_t)gch * a.num_k_heads + hk].Kt[0][0];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             *reinterpret_cast<uint4 *>(&sm.K[tok][32 * part + 8 * m]) = kv[m];
@@ -176,7 +191,6 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
             for (int e = 0; e < 8; ++e) {
                 skk = __builtin_fmaf(kf[e], kf[e], skk);
                 sqq = __builtin_fmaf(qf[e], qf[e], sqq);
-                if (write_kt) ktg[(32 * part + 8 * m + e) * CT + tok] = (__bf16)kf[e];
             }
         }
         skk = group_sum<4>(skk);
@@ -211,39 +225,54 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
         rec->u2f[t] = expf(lamC - lam) * rk;
         rec->gC[t] = expf(lamC);
     }
+    // K^T for the scan (once per q/k head): lane pair per dim d, 32 tokens each
+    if ((h % grp) == 0) {
+        const int d = tid >> 1, half = tid & 1;
+        bf16x8 col[4];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) col[j >> 3][j & 7] = sm.K[32 * half + j][d];
+        uint4 *dst = reinterpret_cast<uint4 *>(&kts[(int64_t)gch * a.num_k_heads + hk].Kt[d][32 * half]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) dst[m] = __builtin_bit_cast(uint4, col[m]);
+    }
 
-    // ---- stage 1: K K^T -> A (fp32, LDS), Q K^T -> P (hi/lo, workspace)
+    // ---- stage 1: tiles (i-tile c, t-tile w) of K K^T and K Q^T, laid out
+    // so each lane holds 4 consecutive i of one row t of A and of P:
+    // A (fp32) into LDS, P (hi/lo) to the workspace with 8-byte stores
+    {
+        const int t = 16 * w + lr;
+        const float lam_t = sm.lam[t], beta_t = sm.beta[t], rk_t = sm.rk[t], rq_t = sm.rq[t];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int ii = 16 * c + lr;
-        if (c > w) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * w + 4 * lq + i;
-                rec->Phi[t][ii] = (__bf16)0.f;
-                rec->Plo[t][ii] = (__bf16)0.f;
+        for (int c = 0; c < 4; ++c) {
+            const int i0 = 16 * c + 4 * lq;
+            if (c > w) {
+                const bf16x4 z = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+                st4(&rec->Phi[t][i0], z);
+                st4(&rec->Plo[t][i0], z);
+                continue;
             }
-            continue;
-        }
-        f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+            f32x4 kk = {0.f, 0.f, 0.f, 0.f}, kq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < DKC / 32; ++ks) {
-            const bf16x8 ak = frag(&sm.K[0][0], LDK, 16 * w, 32 * ks, lane);
-            const bf16x8 aq = frag(&sm.Q[0][0], LDK, 16 * w, 32 * ks, lane);
-            const bf16x8 bk = frag(&sm.K[0][0], LDK, 16 * c, 32 * ks, lane);
-            kk = mma(ak, bk, kk);
-            qk = mma(aq, bk, qk);
-        }
-        const float lam_i = sm.lam[ii], rk_i = sm.rk[ii];
+            for (int ks = 0; ks < DKC / 32; ++ks) {
+                const bf16x8 ai = frag(&sm.K[0][0], LDK, 16 * c, 32 * ks, lane);
+                const bf16x8 bk = frag(&sm.K[0][0], LDK, 16 * w, 32 * ks, lane);
+                const bf16x8 bq = frag(&sm.Q[0][0], LDK, 16 * w, 32 * ks, lane);
+                kk = mma(ai, bk, kk);
+                kq = mma(ai, bq, kq);
+            }
+            f32x4 av, pv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 16 * w + 4 * lq + i;
-            const float decay = ii <= t ? expf(sm.lam[t] - lam_i) : 0.f;
-            sm.A[t][ii] = ii < t ? sm.beta[t] * sm.rk[t] * rk_i * decay * kk[i] : 0.f;
-            __bf16 hi, lo;
-            split(ii <= t ? a.scale * sm.rq[t] * rk_i * decay * qk[i] : 0.f, hi, lo);
-            rec->Phi[t][ii] = hi;
-            rec->Plo[t][ii] = lo;
+            for (int e = 0; e < 4; ++e) {
+                const int i = i0 + e;
+                const float decay = i <= t ? expf(lam_t - sm.lam[i]) : 0.f;
+                av[e] = i < t ? beta_t * rk_t * sm.rk[i] * decay * kk[e] : 0.f;
+                pv[e] = i <= t ? a.scale * rq_t * sm.rk[i] * decay * kq[e] : 0.f;
+            }
+            *reinterpret_cast<f32x4 *>(&sm.A[t][i0]) = av;
+            bf16x4 ph, pl;
+            split4(pv, ph, pl);
+            st4(&rec->Phi[t][i0], ph);
+            st4(&rec->Plo[t][i0], pl);
         }
     }
     __syncthreads();
@@ -307,92 +336,28 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
 // ---------------------------------------------------------------------------
 // scan: one workgroup per (sequence, v-head, 32 v rows)
 // ---------------------------------------------------------------------------
+// Only data that crosses waves lives in LDS (the state entering the chunk
+// and R, U, U'); every MFMA operand a wave owns (its K / Q / T / P rows, its
+// K^T rows) is loaded straight from global memory / L2 into registers one
+// phase ahead of use.  45 KB of LDS lets three workgroups share a CU.
 struct ScanSmem {
-    __bf16 K[CT][LDK];
-    __bf16 Q[CT][LDK];
-    __bf16 Kt[DKC][LDT];
-    __bf16 Shi[DVB][LDK], Slo[DVB][LDK];
-    __bf16 Thi[CT][LDT], Tlo[CT][LDT];
-    __bf16 Phi[CT][LDT], Plo[CT][LDT];
-    __bf16 Rhi[DVB][LDT], Rlo[DVB][LDT];
-    __bf16 Uhi[DVB][LDT], Ulo[DVB][LDT];
-    __bf16 U2hi[DVB][LDT], U2lo[DVB][LDT];
-    float beta[CT], bgr[CT], sqg[CT], u2f[CT], gC;
+    __bf16 Shi[DVB][LDK], Slo[DVB][LDK];     // S0 [r][d]
+    __bf16 Rhi[DVB][LDT], Rlo[DVB][LDT];     // R^T [r][t]
+    __bf16 Uhi[DVB][LDT], Ulo[DVB][LDT];     // U^T [r][t]
+    __bf16 U2hi[DVB][LDT], U2lo[DVB][LDT];   // U'^T [r][t]
 };
 
-// one chunk's inputs in flight, in registers
-struct ChunkIn {
-    uint4 k[4], q[4];      // token tid/4, dims 32*(tid%4) ..
-    uint4 kt[4];           // K^T row (tid*4 + m) / 8, segment (tid*4 + m) % 8
-    uint4 t[4], p[4];      // T hi/lo, P hi/lo: 16-byte pieces tid + 256*m
-    float sc;              // one per-token scalar
-    float gc;              // G_C (thread 0)
-    float v[2][4];         // v in the accumulator layout
-};
+// operand fragment straight from global memory (row-major, `ld` elements)
+__device__ __forceinline__ bf16x8 gfrag(const __bf16 *base, int64_t ld, int row, int k0, int lane) {
+    return *reinterpret_cast<const bf16x8 *>(base + (int64_t)row * ld + k0 + 8 * (lane >> 4));
+}
 
 __device__ __forceinline__ uint4 mask4(bool keep, const uint4 &v) {
     return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
 }
 
-// Every load reads a valid address (rows past the chunk end re-read its last
-// row) and padding is masked on values, so no load is predicated -- that
-// keeps the in-flight chunk in registers.
-__device__ __forceinline__ void fetch_chunk(ChunkIn &in, const RecurrentArgs &a, const ChunkRec *rec,
-                                            const KtRec *kt, int t0, int n, int h, int hk, int vb, int tid) {
-    const int tok = tid >> 2, part = tid & 3;
-    const bool live = tok < n;
-    const int row = t0 + min(tok, n - 1);
-    const uint4 *kp = reinterpret_cast<const uint4 *>(a.k + (int64_t)row * a.k_stride + hk * DKC + 32 * part);
-    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + (int64_t)row * a.q_stride + hk * DKC + 32 * part);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        in.k[m] = mask4(live, kp[m]);
-        in.q[m] = mask4(live, qp[m]);
-    }
-    const uint4 *ktp = reinterpret_cast<const uint4 *>(&kt->Kt[0][0]);
-    const uint4 *tp = reinterpret_cast<const uint4 *>(&rec->Thi[0][0]);   // Thi then Tlo
-    const uint4 *pp = reinterpret_cast<const uint4 *>(&rec->Phi[0][0]);   // Phi then Plo
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        in.kt[m] = ktp[tid * 4 + m];
-        in.t[m] = tp[tid + NTH * m];
-        in.p[m] = pp[tid + NTH * m];
-    }
-    const float *scal = &rec->beta[0];
-    in.sc = scal[tid];                            // beta, bgr, sqg, u2f: 4 x 64
-    in.gc = rec->gC[0];
-    const int lane = tid & 63, w = tid >> 6, lr = lane & 15, lq = lane >> 4;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tt = 16 * w + 4 * lq + i;
-            const float vf = bf16_to_f32(a.v[(int64_t)(t0 + min(tt, n - 1)) * a.v_stride + (int64_t)h * a.dv +
-                                             vb * DVB + 16 * rt + lr]);
-            in.v[rt][i] = tt < n ? vf : 0.f;
-        }
-}
-
-__device__ __forceinline__ void stage_chunk(ScanSmem &sm, const ChunkIn &in, int tid) {
-    const int tok = tid >> 2, part = tid & 3;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        *reinterpret_cast<uint4 *>(&sm.K[tok][32 * part + 8 * m]) = in.k[m];
-        *reinterpret_cast<uint4 *>(&sm.Q[tok][32 * part + 8 * m]) = in.q[m];
-        const int e = tid * 4 + m;                 // K^T: 128 rows x 8 pieces
-        *reinterpret_cast<uint4 *>(&sm.Kt[e >> 3][(e & 7) * 8]) = in.kt[m];
-        const int f = tid + NTH * m;               // T/P: 2 x 64 rows x 8 pieces
-        const int row = (f >> 3) & (CT - 1), col = (f & 7) * 8;
-        if (f < CT * 8) {
-            *reinterpret_cast<uint4 *>(&sm.Thi[row][col]) = in.t[m];
-            *reinterpret_cast<uint4 *>(&sm.Phi[row][col]) = in.p[m];
-        } else {
-            *reinterpret_cast<uint4 *>(&sm.Tlo[row][col]) = in.t[m];
-            *reinterpret_cast<uint4 *>(&sm.Plo[row][col]) = in.p[m];
-        }
-    }
-    if (tid < 4 * CT) (&sm.beta[0])[tid] = in.sc;   // beta, bgr, sqg, u2f are contiguous
-    if (tid == 0) sm.gC = in.gc;
+__device__ __forceinline__ bf16x8 maskf(bool keep, const bf16x8 &v) {
+    return __builtin_bit_cast(bf16x8, mask4(keep, __builtin_bit_cast(uint4, v)));
 }
 
 __global__ __launch_bounds__(NTH) void chunk_scan_kernel(RecurrentArgs a, const ChunkRec *recs, const KtRec *kts,
@@ -415,154 +380,226 @@ __global__ __launch_bounds__(NTH) void chunk_scan_kernel(RecurrentArgs a, const 
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lq = lane >> 4;
+    const int kh_off = hk * DKC;
+    const __bf16 *kbase = reinterpret_cast<const __bf16 *>(a.k) + kh_off;
+    const __bf16 *qbase = reinterpret_cast<const __bf16 *>(a.q) + kh_off;
 
-    // state slice in the accumulator layout: tile q = 2*rt + (dt - 2w),
-    // element i -> row 16 rt + 4 lq + i, column 16 dt + lr
+    // the state slice, transposed, in the accumulator layout of S^T tiles
+    // (d-tile dt, v-row tile rt): tile q = 2*rt + (dt - 2w); lane holds
+    // S[16 rt + lr][16 dt + 4 lq .. +3] -- four consecutive dims of one row
     float *S_g = a.state + ((int64_t)slot * HV + h) * (int64_t)a.dv * DKC + (int64_t)vb * DVB * DKC;
     f32x4 S[4];
     const bool init = a.has_init == nullptr || a.has_init[s] != 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int rt = q >> 1, dt = 2 * w + (q & 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[q][i] = init ? S_g[(16 * rt + 4 * lq + i) * DKC + 16 * dt + lr] : 0.f;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        S[q] = init ? *reinterpret_cast<const f32x4 *>(&S_g[(16 * rt + lr) * DKC + 16 * dt + 4 * lq]) : z;
     }
 
-    ChunkIn in;
-    fetch_chunk(in, a, recs + (int64_t)gch * HV + h, kts + (int64_t)gch * a.num_k_heads + hk, t_begin,
-                min(CT, t_end - t_begin), h, hk, vb, tid);
+    // per-lane operands of one chunk; each group is (re)loaded right after
+    // its last use, for the next chunk
+    bf16x8 kf[4], qf[4];                // K, Q rows 16w + lr, dims 32 ks + 8 lq ..
+    f32x4 sb, sbgr, ssqg;               // beta, bgr, sqg of tokens 16w + 4lq + i
+    uint16_t vraw[2][4];                // v of tokens 16w + 4lq + i, rows 16 rt + lr
+    bf16x8 th[2], tl[2];                // T rows 16w + lr, cols 32 ks + 8 lq ..
+    f32x4 su2;                          // u2f of tokens 16w + 4lq + i
+    bf16x8 ph[2], pl[2], ktf[2][2];     // P rows; K^T rows 16 dt + lr
+    float gC;
 
-    for (int t0 = t_begin; t0 < t_end; t0 += CT, ++gch) {
-        const int n = min(CT, t_end - t0);
-
-        // ---- this chunk's inputs and the state entering it into LDS
-        stage_chunk(sm, in, tid);
-        float vv[2][4];
+    auto load_y = [&](int c_t0, int c_n, const ChunkRec *rec) {
+        const int row = c_t0 + min(16 * w + lr, c_n - 1);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            kf[ks] = gfrag(kbase, a.k_stride, row, 32 * ks, lane);
+            qf[ks] = gfrag(qbase, a.q_stride, row, 32 * ks, lane);
+        }
+        const int t4 = 16 * w + 4 * lq;
+        sb = *reinterpret_cast<const f32x4 *>(&rec->beta[t4]);
+        sbgr = *reinterpret_cast<const f32x4 *>(&rec->bgr[t4]);
+        ssqg = *reinterpret_cast<const f32x4 *>(&rec->sqg[t4]);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) vv[rt][i] = in.v[rt][i];
+            for (int i = 0; i < 4; ++i)
+                vraw[rt][i] = a.v[(int64_t)(c_t0 + min(t4 + i, c_n - 1)) * a.v_stride + (int64_t)h * a.dv +
+                                  vb * DVB + 16 * rt + lr];
+    };
+    auto load_t = [&](const ChunkRec *rec) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            th[ks] = gfrag(&rec->Thi[0][0], CT, 16 * w + lr, 32 * ks, lane);
+            tl[ks] = gfrag(&rec->Tlo[0][0], CT, 16 * w + lr, 32 * ks, lane);
+        }
+        su2 = *reinterpret_cast<const f32x4 *>(&rec->u2f[16 * w + 4 * lq]);
+    };
+    auto load_p = [&](const ChunkRec *rec, const KtRec *kt) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            ph[ks] = gfrag(&rec->Phi[0][0], CT, 16 * w + lr, 32 * ks, lane);
+            pl[ks] = gfrag(&rec->Plo[0][0], CT, 16 * w + lr, 32 * ks, lane);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) ktf[j][ks] = gfrag(&kt->Kt[0][0], CT, 16 * (2 * w + j) + lr, 32 * ks, lane);
+        }
+        gC = rec->gC[0];
+    };
+
+    {
+        const ChunkRec *rec = recs + (int64_t)gch * HV + h;
+        const int n0 = min(CT, t_end - t_begin);
+        load_y(t_begin, n0, rec);
+        load_t(rec);
+        load_p(rec, kts + (int64_t)gch * a.num_k_heads + hk);
+    }
+
+    for (int t0 = t_begin; t0 < t_end; t0 += CT, ++gch) {
+        const int n = min(CT, t_end - t0);
+        const bool more = t0 + CT < t_end;
+        const int n_next = more ? min(CT, t_end - t0 - CT) : 1;
+        const ChunkRec *rec_next = recs + (int64_t)(gch + 1) * HV + h;
+        const KtRec *kt_next = kts + (int64_t)(gch + 1) * a.num_k_heads + hk;
+
+        // ---- the state entering the chunk -> LDS (hi/lo)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int rt = q >> 1, dt = 2 * w + (q & 1);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                __bf16 hi, lo;
-                split(S[q][i], hi, lo);
-                sm.Shi[16 * rt + 4 * lq + i][16 * dt + lr] = hi;
-                sm.Slo[16 * rt + 4 * lq + i][16 * dt + lr] = lo;
-            }
+            bf16x4 hi, lo;
+            split4(S[q], hi, lo);
+            st4(&sm.Shi[16 * rt + lr][16 * dt + 4 * lq], hi);
+            st4(&sm.Slo[16 * rt + lr][16 * dt + 4 * lq], lo);
         }
         __syncthreads();
-        // the next chunk's inputs travel while this one computes
-        if (t0 + CT < t_end)
-            fetch_chunk(in, a, recs + (int64_t)(gch + 1) * HV + h, kts + (int64_t)(gch + 1) * a.num_k_heads + hk,
-                        t0 + CT, min(CT, t_end - t0 - CT), h, hk, vb, tid);
 
         // ---- R = b v - bgr (K S0^T) -> LDS;  o part = sqg (Q S0^T)
+        const bool live = 16 * w + lr < n;
         f32x4 O[2];
+        {
+            bf16x8 ka[4], qa[4];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            f32x4 yk = {0.f, 0.f, 0.f, 0.f}, yq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < DKC / 32; ++ks) {
-                const bf16x8 ak = frag(&sm.K[0][0], LDK, 16 * w, 32 * ks, lane);
-                const bf16x8 aq = frag(&sm.Q[0][0], LDK, 16 * w, 32 * ks, lane);
-                const bf16x8 bh = frag(&sm.Shi[0][0], LDK, 16 * rt, 32 * ks, lane);
-                const bf16x8 bl = frag(&sm.Slo[0][0], LDK, 16 * rt, 32 * ks, lane);
-                yk = mma(ak, bh, yk);
-                yk = mma(ak, bl, yk);
-                yq = mma(aq, bh, yq);
-                yq = mma(aq, bl, yq);
+            for (int ks = 0; ks < 4; ++ks) {
+                ka[ks] = maskf(live, kf[ks]);
+                qa[ks] = maskf(live, qf[ks]);
             }
+            float vv[2][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * w + 4 * lq + i;
-                const float r = sm.beta[t] * vv[rt][i] - sm.bgr[t] * yk[i];
-                __bf16 hi, lo;
-                split(r, hi, lo);
-                sm.Rhi[16 * rt + lr][t] = hi;
-                sm.Rlo[16 * rt + lr][t] = lo;
-                O[rt][i] = sm.sqg[t] * yq[i];
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vv[rt][i] = 16 * w + 4 * lq + i < n ? bf16_to_f32(vraw[rt][i]) : 0.f;
+            const f32x4 b = sb, bgr = sbgr, sqg = ssqg;
+            if (more) load_y(t0 + CT, n_next, rec_next);     // next chunk's K, Q, v, factors
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                f32x4 yk = {0.f, 0.f, 0.f, 0.f}, yq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < DKC / 32; ++ks) {
+                    const bf16x8 bh = frag(&sm.Shi[0][0], LDK, 16 * rt, 32 * ks, lane);
+                    const bf16x8 bl = frag(&sm.Slo[0][0], LDK, 16 * rt, 32 * ks, lane);
+                    yk = mma(ka[ks], bh, yk);
+                    yq = mma(qa[ks], bh, yq);
+                    yk = mma(ka[ks], bl, yk);
+                    yq = mma(qa[ks], bl, yq);
+                }
+                f32x4 r;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    r[i] = b[i] * vv[rt][i] - bgr[i] * yk[i];
+                    O[rt][i] = sqg[i] * yq[i];
+                }
+                bf16x4 hi, lo;
+                split4(r, hi, lo);
+                st4(&sm.Rhi[16 * rt + lr][16 * w + 4 * lq], hi);
+                st4(&sm.Rlo[16 * rt + lr][16 * w + 4 * lq], lo);
             }
         }
         __syncthreads();
 
         // ---- U = T R (token tile w; T lower triangular) -> LDS, with U' = u2f U
+        {
+            const bf16x8 t_h0 = th[0], t_h1 = th[1], t_l0 = tl[0], t_l1 = tl[1];
+            const f32x4 u2f = su2;
+            if (more) load_t(rec_next);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            f32x4 u = {0.f, 0.f, 0.f, 0.f};
+            for (int rt = 0; rt < 2; ++rt) {
+                f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (ks > (w >> 1)) break;
-                const bf16x8 ah = frag(&sm.Thi[0][0], LDT, 16 * w, 32 * ks, lane);
-                const bf16x8 al = frag(&sm.Tlo[0][0], LDT, 16 * w, 32 * ks, lane);
-                const bf16x8 bh = frag(&sm.Rhi[0][0], LDT, 16 * rt, 32 * ks, lane);
-                const bf16x8 bl = frag(&sm.Rlo[0][0], LDT, 16 * rt, 32 * ks, lane);
-                u = mma(ah, bh, u);
-                u = mma(ah, bl, u);
-                u = mma(al, bh, u);
-            }
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (ks > (w >> 1)) break;
+                    const bf16x8 bh = frag(&sm.Rhi[0][0], LDT, 16 * rt, 32 * ks, lane);
+                    const bf16x8 bl = frag(&sm.Rlo[0][0], LDT, 16 * rt, 32 * ks, lane);
+                    const bf16x8 ah = ks ? t_h1 : t_h0, al = ks ? t_l1 : t_l0;
+                    u = mma(ah, bh, u);
+                    u = mma(ah, bl, u);
+                    u = mma(al, bh, u);
+                }
+                f32x4 u2;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * w + 4 * lq + i;
-                __bf16 hi, lo;
-                split(u[i], hi, lo);
-                sm.Uhi[16 * rt + lr][t] = hi;
-                sm.Ulo[16 * rt + lr][t] = lo;
-                split(sm.u2f[t] * u[i], hi, lo);
-                sm.U2hi[16 * rt + lr][t] = hi;
-                sm.U2lo[16 * rt + lr][t] = lo;
+                for (int i = 0; i < 4; ++i) u2[i] = u2f[i] * u[i];
+                bf16x4 hi, lo;
+                split4(u, hi, lo);
+                st4(&sm.Uhi[16 * rt + lr][16 * w + 4 * lq], hi);
+                st4(&sm.Ulo[16 * rt + lr][16 * w + 4 * lq], lo);
+                split4(u2, hi, lo);
+                st4(&sm.U2hi[16 * rt + lr][16 * w + 4 * lq], hi);
+                st4(&sm.U2lo[16 * rt + lr][16 * w + 4 * lq], lo);
             }
         }
         __syncthreads();
 
-        // ---- o = part + P U -> output;  S = G_C S + U'^T K
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            f32x4 acc = O[rt];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (ks > (w >> 1)) break;
-                const bf16x8 ah = frag(&sm.Phi[0][0], LDT, 16 * w, 32 * ks, lane);
-                const bf16x8 al = frag(&sm.Plo[0][0], LDT, 16 * w, 32 * ks, lane);
-                const bf16x8 bh = frag(&sm.Uhi[0][0], LDT, 16 * rt, 32 * ks, lane);
-                const bf16x8 bl = frag(&sm.Ulo[0][0], LDT, 16 * rt, 32 * ks, lane);
-                acc = mma(ah, bh, acc);
-                acc = mma(ah, bl, acc);
-                acc = mma(al, bh, acc);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * w + 4 * lq + i;
-                if (t < n)
-                    a.o[(int64_t)(t0 + t) * a.o_stride + (int64_t)h * a.dv + vb * DVB + 16 * rt + lr] =
-                        f32_to_bf16(acc[i]);
-            }
-        }
-        const float gC = sm.gC;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int rt = q >> 1, dt = 2 * w + (q & 1);
-            f32x4 acc = S[q] * gC;
+        // ---- o = part + P U -> output;  S^T = G_C S^T + K^T U'
+        {
+            bf16x8 p_h[2], p_l[2], kt_f[2][2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 ah = frag(&sm.U2hi[0][0], LDT, 16 * rt, 32 * ks, lane);
-                const bf16x8 al = frag(&sm.U2lo[0][0], LDT, 16 * rt, 32 * ks, lane);
-                const bf16x8 bk = frag(&sm.Kt[0][0], LDT, 16 * dt, 32 * ks, lane);
-                acc = mma(ah, bk, acc);
-                acc = mma(al, bk, acc);
+                p_h[ks] = ph[ks];
+                p_l[ks] = pl[ks];
+                kt_f[0][ks] = ktf[0][ks];
+                kt_f[1][ks] = ktf[1][ks];
             }
-            S[q] = acc;
+            const float g_c = gC;
+            if (more) load_p(rec_next, kt_next);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                f32x4 acc = O[rt];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (ks > (w >> 1)) break;
+                    const bf16x8 bh = frag(&sm.Uhi[0][0], LDT, 16 * rt, 32 * ks, lane);
+                    const bf16x8 bl = frag(&sm.Ulo[0][0], LDT, 16 * rt, 32 * ks, lane);
+                    acc = mma(p_h[ks], bh, acc);
+                    acc = mma(p_h[ks], bl, acc);
+                    acc = mma(p_l[ks], bh, acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * w + 4 * lq + i;
+                    if (t < n)
+                        a.o[(int64_t)(t0 + t) * a.o_stride + (int64_t)h * a.dv + vb * DVB + 16 * rt + lr] =
+                            f32_to_bf16(acc[i]);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int rt = q >> 1, j = q & 1;
+                f32x4 acc = S[q] * g_c;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8 bh = frag(&sm.U2hi[0][0], LDT, 16 * rt, 32 * ks, lane);
+                    const bf16x8 bl = frag(&sm.U2lo[0][0], LDT, 16 * rt, 32 * ks, lane);
+                    acc = mma(kt_f[j][ks], bh, acc);
+                    acc = mma(kt_f[j][ks], bl, acc);
+                }
+                S[q] = acc;
+            }
         }
-        __syncthreads();
+        // no barrier: the next chunk writes S (read only before the second
+        // barrier above), then R, U, U' only after barriers every wave passes
+        // once it is done with this chunk
     }
 
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int rt = q >> 1, dt = 2 * w + (q & 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S_g[(16 * rt + 4 * lq + i) * DKC + 16 * dt + lr] = S[q][i];
+        *reinterpret_cast<f32x4 *>(&S_g[(16 * rt + lr) * DKC + 16 * dt + 4 * lq]) = S[q];
     }
 }
 
