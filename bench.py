@@ -11,10 +11,10 @@ in the 256 MB Infinity Cache, as in a model with several GDN layers.
 
 Per engine step: the host builds the exact (sequence, 8-token chunk)
 descriptors once (gdn_build_conv_chunks) and uploads them once; then for every
-layer: conv update for the decode rows, varlen conv for the prefill rows,
-the fused recurrence for the decodes and the chunkwise (matrix-core) form of
-the same rule for the prefill chunks (q, k, v are column views of the conv
-output).  Inputs are resident in HBM before the
+layer: one fused launch for the decode rows (conv update + gated delta rule,
+gdn_fused_conv_decode), the varlen conv for the prefill rows and the
+chunkwise (matrix-core) form of the rule for the prefill chunks (q, k, v are
+column views of the conv output).  Inputs are resident in HBM before the
 timed region; every call goes through the C ABI on torch's current stream.
 
 Output: one JSON line.  ``value`` is GDN-layer tokens per second (tokens x
@@ -75,6 +75,14 @@ def bytes_conv_varlen(tokens, seqs, seqs_with_init, n_chunks):
 
 def bytes_conv_update(batch):
     return batch * (2 * C * 2 + 2 * 3 * C * 2 + 4) + C * K * 2 + C * 2
+
+
+def bytes_fused_decode(batch):
+    state = D * D * 4 * HV
+    return (batch * (C * 2 + 2 * 3 * C * 2 + 4)        # x, conv_state read + write, slot index
+            + C * K * 2 + C * 2                         # conv weights, bias
+            + batch * 2 * state                         # recurrent state read + write
+            + batch * (HV * D * 2 + HV * 8))            # o, g, beta
 
 
 def bytes_recurrent(tokens, seqs_with_state_read, seqs):
@@ -211,11 +219,14 @@ def main():
             G, B = ly["g"].data_ptr(), ly["beta"].data_ptr()
             yq, yk, yv = Y, Y + HK * D * 2, Y + 2 * HK * D * 2
             if nd:
+                # decode rows: conv update fused with the recurrence (one launch)
                 di = dec_idx_d.data_ptr() + int(dec_off[si]) * i32
-                calls.append(("conv_update", lib.gdn_causal_conv1d_update,
+                calls.append(("fused_decode", lib.gdn_fused_conv_decode,
                               (X + off * C * 2, C, ly["w"].data_ptr(), ly["b"].data_ptr(), ly["cs"].data_ptr(),
-                               SLOTS, di, Y, C, nd, C, K, 1, sptr),
-                              bytes_conv_update(nd), 0.0))
+                               SLOTS, G + off * HV * 4, B + off * HV * 4, ly["state"].data_ptr(), SLOTS, di,
+                               O + off * HV * D * 2, HV * D, None, 0, nd, HK, HV, D, D, 1, ctypes.c_float(1.0),
+                               1, sptr),
+                              bytes_fused_decode(nd), flops_recurrent(nd)))
             if npf:
                 qd = qsl_d.data_ptr() + int(qsl_off[si]) * i32
                 pi = pidx_d.data_ptr() + int(pidx_off[si]) * i32
@@ -227,12 +238,6 @@ def main():
                                ly["cs"].data_ptr(), SLOTS, qd, pi, ph, cd, n_chunks[si], Y + nd * C * 2, C,
                                npf, tp, C, K, 1, sptr),
                               bytes_conv_varlen(tp, npf, n_init, n_chunks[si]), 0.0))
-            if nd:
-                calls.append(("recurrent_decode", lib.gdn_fused_recurrent_decode,
-                              (yq, C, yk, C, yv, C, G + off * HV * 4, B + off * HV * 4, ly["state"].data_ptr(),
-                               SLOTS, None, di, None, O + off * HV * D * 2, HV * D, nd, nd, HK, HV, D, D,
-                               ctypes.c_float(1.0), 1, sptr),
-                              bytes_recurrent(nd, nd, nd), flops_recurrent(nd)))
             if npf:
                 po = off + nd
                 calls.append(("recurrent_chunk", lib.gdn_chunk_gated_delta_rule,
@@ -279,7 +284,7 @@ def main():
         n = sum(1 for calls in plans for c in calls if c[0] == kind)
         return n, nb, nf
 
-    kinds = ["conv_varlen", "conv_update", "recurrent_decode", "recurrent_chunk"]
+    kinds = ["conv_varlen", "fused_decode", "recurrent_chunk"]
 
     # ---- warm-up, then one instrumented pass (untimed) for the per-kernel shares
     for _ in range(args.warmup):

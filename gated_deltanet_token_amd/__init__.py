@@ -27,7 +27,7 @@ CONV_WIDTH = 4
 # every entry point declared in include/gdn.h
 EXPORTS = ("gdn_last_error", "gdn_build_conv_chunks", "gdn_causal_conv1d_varlen",
            "gdn_causal_conv1d_update", "gdn_fused_recurrent_decode", "gdn_chunk_gated_delta_rule",
-           "gdn_chunk_workspace_size")
+           "gdn_fused_conv_decode", "gdn_chunk_workspace_size")
 
 
 class GDNError(RuntimeError):
@@ -49,8 +49,11 @@ def _bind(path):
                                                i32, i32, i32, i32, i32, i32, f32, i32, P]
     lib.gdn_chunk_gated_delta_rule.argtypes = [P, i64, P, i64, P, i64, P, P, P, i32, P, P, P, P, i64,
                                                i32, i32, i32, i32, i32, i32, P, ctypes.c_size_t, f32, i32, P]
-    for name in EXPORTS[1:-1]:
-        getattr(lib, name).restype = ctypes.c_int
+    for name in EXPORTS[1:]:
+        if name != "gdn_chunk_workspace_size":
+            getattr(lib, name).restype = ctypes.c_int
+    lib.gdn_fused_conv_decode.argtypes = [P, i64, P, P, P, i32, P, P, P, i32, P, P, i64, P, i64,
+                                          i32, i32, i32, i32, i32, i32, f32, i32, P]
     lib.gdn_chunk_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.gdn_chunk_workspace_size.restype = ctypes.c_size_t
     return lib
@@ -233,3 +236,27 @@ def gdn_chunk_gated_delta_rule(q, k, v, g, beta, state, state_indices, o, query_
     omitted, torch allocates one for the call."""
     _recurrent("gdn_chunk_gated_delta_rule", q, k, v, g, beta, state, state_indices, o, query_start_loc,
                has_initial_state, scale, qk_l2norm, stream, workspace)
+
+
+def gdn_fused_conv_decode(x, conv_weight, conv_bias, conv_state, g, beta, state, state_indices, o,
+                          num_k_heads, head_k_dim, y=None, silu=True, scale=1.0, qk_l2norm=True,
+                          stream=None):
+    """Decode step: conv update of x (q | k | v channels) fused with the gated
+    delta rule on its output; see gdn.h.  o: bf16 [B][HV][dv]; y optional."""
+    torch = _torch()
+    for t, n in ((x, "x"), (conv_weight, "conv_weight"), (conv_bias, "conv_bias"),
+                 (conv_state, "conv_state"), (o, "o"), (y, "y")):
+        _dtype(t, torch.bfloat16, n)
+    for t, n in ((g, "g"), (beta, "beta"), (state, "state")):
+        _dtype(t, torch.float32, n)
+    _dtype(state_indices, torch.int32, "state_indices")
+    if not (g.is_contiguous() and beta.is_contiguous() and state.is_contiguous()):
+        raise ValueError("g, beta and state must be contiguous")
+    B = x.shape[0]
+    HV, dv = o.shape[1], o.shape[2]
+    rc = lib.gdn_fused_conv_decode(
+        _ptr(x), _rows(x, "x"), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state), conv_state.shape[0],
+        _ptr(g), _ptr(beta), _ptr(state), state.shape[0], _ptr(state_indices), _ptr(o), _heads(o, "o"),
+        _ptr(y), 0 if y is None else _rows(y, "y"), B, num_k_heads, HV, head_k_dim, dv, int(bool(silu)),
+        float(scale), int(bool(qk_l2norm)), _stream(stream))
+    _check(rc, "gdn_fused_conv_decode")

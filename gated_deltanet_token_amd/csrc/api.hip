@@ -218,3 +218,47 @@ GDN_EXPORT int gdn_chunk_gated_delta_rule(const gdn_bf16 *q, int64_t q_stride, c
     return hip_status(gdn::launch_chunk_recurrent(a, workspace, num_tokens, (hipStream_t)stream),
                       "chunk recurrent launch");
 }
+
+GDN_EXPORT int gdn_fused_conv_decode(const gdn_bf16 *x, int64_t x_stride, const gdn_bf16 *conv_weight,
+                                     const gdn_bf16 *conv_bias, gdn_bf16 *conv_state, int32_t num_conv_slots,
+                                     const float *g, const float *beta, float *state, int32_t num_slots,
+                                     const int32_t *state_indices, gdn_bf16 *o, int64_t o_stride, gdn_bf16 *y,
+                                     int64_t y_stride, int32_t batch, int32_t num_k_heads, int32_t num_v_heads,
+                                     int32_t head_k_dim, int32_t head_v_dim, int32_t silu, float scale,
+                                     int32_t qk_l2norm, void *stream) {
+    if (!x || !conv_weight || !conv_state || !g || !beta || !state || !state_indices || !o)
+        return fail(GDN_ERR_INVALID, "x, conv_weight, conv_state, g, beta, state, state_indices and o are required");
+    if (batch < 0) return fail(GDN_ERR_INVALID, "negative batch");
+    if (num_conv_slots < 1 || num_slots < 1) return fail(GDN_ERR_INVALID, "slot counts must be >= 1");
+    if (num_k_heads <= 0 || num_v_heads <= 0 || num_v_heads % num_k_heads)
+        return fail(GDN_ERR_INVALID, "num_v_heads must be a positive multiple of num_k_heads");
+    if (head_k_dim != 16 && head_k_dim != 32 && head_k_dim != 64 && head_k_dim != 128)
+        return fail(GDN_ERR_UNSUPPORTED, "head_k_dim %d: supported 16, 32, 64, 128", head_k_dim);
+    if (head_v_dim <= 0 || head_v_dim % 8 || head_v_dim > 256)
+        return fail(GDN_ERR_UNSUPPORTED, "head_v_dim %d: must be a multiple of 8 up to 256", head_v_dim);
+    const int64_t grp = num_v_heads / num_k_heads;
+    if (2 * head_k_dim + grp * head_v_dim > gdn::fused_max_group_channels())
+        return fail(GDN_ERR_UNSUPPORTED, "a q/k head group reads more than %d conv channels",
+                    gdn::fused_max_group_channels());
+    const int64_t channels = 2 * (int64_t)num_k_heads * head_k_dim + (int64_t)num_v_heads * head_v_dim;
+    const int64_t v_w = (int64_t)num_v_heads * head_v_dim;
+    if (channels > INT32_MAX) return fail(GDN_ERR_INVALID, "channel count overflows int32");
+    if (x_stride < channels || (y && y_stride < channels) || o_stride < v_w)
+        return fail(GDN_ERR_INVALID, "a row stride is smaller than its row");
+    if (x_stride % 8 || (y && y_stride % 8) || o_stride % 8)
+        return fail(GDN_ERR_UNSUPPORTED, "strides must be multiples of 8 elements");
+    if (!aligned16(x) || !aligned16(conv_weight) || (conv_bias && !aligned16(conv_bias)) || !aligned16(conv_state) ||
+        !aligned16(state) || !aligned16(o) || (y && !aligned16(y)))
+        return fail(GDN_ERR_UNSUPPORTED, "x, conv_weight, conv_bias, conv_state, state, o and y must be 16-byte aligned");
+    const Span xs = row_span(x, batch, x_stride, channels, 2);
+    if (overlap(xs, row_span(o, batch, o_stride, v_w, 2)))
+        return fail(GDN_ERR_INVALID, "o overlaps x");
+    if (y && (overlap(xs, row_span(y, batch, y_stride, channels, 2)) ||
+              overlap(row_span(o, batch, o_stride, v_w, 2), row_span(y, batch, y_stride, channels, 2))))
+        return fail(GDN_ERR_INVALID, "y overlaps x or o");
+    if (batch == 0) return ok();
+    gdn::FusedDecodeArgs a{x, x_stride, conv_weight, conv_bias, conv_state, (int)channels, g, beta, state,
+                           state_indices, o, o_stride, y, y_stride, batch, num_k_heads, num_v_heads, head_k_dim,
+                           head_v_dim, scale, qk_l2norm, silu};
+    return hip_status(gdn::launch_fused_conv_decode(a, (hipStream_t)stream), "fused conv decode launch");
+}

@@ -64,9 +64,36 @@ struct RecurrentArgs {
     int l2norm;
 };
 
+struct FusedDecodeArgs {
+    const uint16_t *x;           // [batch][x_stride]: q | k | v channels
+    int64_t x_stride;
+    const uint16_t *conv_weight;
+    const uint16_t *conv_bias;
+    uint16_t *conv_state;
+    int channels;                // 2 HK dk + HV dv
+    const float *g;
+    const float *beta;
+    float *state;
+    const int32_t *state_indices;
+    uint16_t *o;
+    int64_t o_stride;
+    uint16_t *y;                 // optional conv output
+    int64_t y_stride;
+    int batch;
+    int num_k_heads;
+    int num_v_heads;
+    int dk;
+    int dv;
+    float scale;
+    int l2norm;
+    int silu;
+};
+
 hipError_t launch_conv_varlen(const ConvVarlenArgs &a, hipStream_t stream);
 hipError_t launch_conv_update(const ConvUpdateArgs &a, hipStream_t stream);
 hipError_t launch_recurrent(const RecurrentArgs &a, hipStream_t stream);
+int fused_max_group_channels();
+hipError_t launch_fused_conv_decode(const FusedDecodeArgs &a, hipStream_t stream);
 // chunkwise form: workspace of chunk_workspace_bytes(...) bytes, 256-byte aligned
 int64_t chunk_workspace_bytes(int num_seqs, int num_tokens, int num_k_heads, int num_v_heads);
 hipError_t launch_chunk_recurrent(const RecurrentArgs &a, void *workspace, int num_tokens, hipStream_t stream);

@@ -17,7 +17,8 @@
 // neighbouring rows.  The state stays in VGPRs for the whole token loop and
 // is read and written exactly once per call.
 //
-// Per token, with raw (unnormalised) q and k and rk, rq the inverse norms:
+// Per token (gdr_math.h), with raw (unnormalised) q and k and rk, rq the
+// inverse norms:
 //   u = (S k) rk, p = (S q) rq           -- one pass over the old row
 //   c = b (v - a u)
 //   S = a S + (c rk) k                   == a S (I - b kh kh^T) + b v kh^T
@@ -28,17 +29,9 @@
 // the decode and the varlen launch shapes give bit-identical tokens.
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdr_math.h"
 
 namespace gdn {
-
-template <int DK>
-struct RowLayout {
-    static constexpr int G = DK >= 32 ? 8 : 4;    // lanes per state row
-    static constexpr int E = DK / G;              // fp32 elements per lane
-    static constexpr int M = E / 4;               // float4 slices per lane
-    static constexpr int RG = 64 / G;             // row groups per wave
-    static_assert(E % 4 == 0 && E >= 4, "head_k_dim must be 16, 32, 64 or 128");
-};
 
 template <int DK, int W, int R>
 struct RecurrentShape {
@@ -145,40 +138,11 @@ __global__ __launch_bounds__(64 * W) void recurrent_kernel(RecurrentArgs a, int 
             qf[4 * m + 2] = bf16_lo(cur.q[m].y);
             qf[4 * m + 3] = bf16_hi(cur.q[m].y);
         }
-        float skk = 0.f, sqq = 0.f, skq = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            skk = __builtin_fmaf(kf[e], kf[e], skk);
-            sqq = __builtin_fmaf(qf[e], qf[e], sqq);
-            skq = __builtin_fmaf(kf[e], qf[e], skq);
-        }
-        skk = group_sum<G>(skk);
-        sqq = group_sum<G>(sqq);
-        skq = group_sum<G>(skq);
-        float rk = 1.f, rq = 1.f;
-        if (a.l2norm) {
-            rk = rsqrtf(skk + 1e-6f);
-            rq = rsqrtf(sqq + 1e-6f);
-        }
+        const TokenFactors f = token_factors<G, E>(kf, qf, a.l2norm != 0);
         const float alpha = expf(gcur);
-        const float beta = bcur;
-        const float kq = skq * rk * rq;
-
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            float u = 0.f, p = 0.f;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                u = __builtin_fmaf(S[r][e], kf[e], u);
-                p = __builtin_fmaf(S[r][e], qf[e], p);
-            }
-            u = group_sum<G>(u) * rk;
-            p = group_sum<G>(p) * rq;
-            const float coef = beta * (bf16_to_f32(vcur[r]) - alpha * u);
-            const float ck = coef * rk;
-#pragma unroll
-            for (int e = 0; e < E; ++e) S[r][e] = __builtin_fmaf(ck, kf[e], alpha * S[r][e]);
-            const float out = a.scale * (alpha * p + coef * kq);
+            const float out = row_step<G, E>(S[r], kf, qf, f, alpha, bcur, bf16_to_f32(vcur[r]), a.scale);
             if (j == 0 && valid[r]) op[(int64_t)t * a.o_stride + row[r]] = f32_to_bf16(out);
         }
 

@@ -11,6 +11,7 @@
  *   gdn_chunk_gated_delta_rule  GPU: the same rule over prefill tokens,
  *                               chunkwise on the matrix cores
  *   gdn_chunk_workspace_size    host: scratch bytes the chunkwise call needs
+ *   gdn_fused_conv_decode       GPU: conv update + gated delta rule, one launch
  *
  * Conventions shared by every call
  * --------------------------------
@@ -270,6 +271,51 @@ int gdn_chunk_gated_delta_rule(const gdn_bf16 *q, int64_t q_stride,
                                int32_t head_k_dim, int32_t head_v_dim,
                                void *workspace, size_t workspace_bytes,
                                float scale, int32_t qk_l2norm, void *stream);
+
+/*
+ * gdn_fused_conv_decode -- one decode step of the whole mixer: the
+ * single-token conv update of every channel fused with the gated delta rule
+ * on its output, in one launch.
+ *
+ * Sources: the width-4 conv and the fused GDN decode of page "RTX 5070 Ti:
+ * close Qwen3.5-4B TTFT, TPOT, and VRAM gaps vs vLLM", section "Existing
+ * evidence"; the rule from Yang, Kautz, Hatamizadeh, "Gated Delta Networks"
+ * (ICLR 2025).
+ *
+ * Equivalent, bit for bit, to
+ *   gdn_causal_conv1d_update(x, ..., y_tmp, ...)      (y_tmp in bf16)
+ *   gdn_fused_recurrent_decode(q = y_tmp[:, 0 : HK dk],
+ *                              k = y_tmp[:, HK dk : 2 HK dk],
+ *                              v = y_tmp[:, 2 HK dk :], ...)
+ * where the conv row is laid out q | k | v (channels = 2 HK dk + HV dv) and
+ * batch row b uses slot state_indices[b] in both pools (negative: skipped).
+ * The conv output is written to y only when y is not NULL.
+ *
+ *   x            bf16 [batch][x_stride]
+ *   conv_weight  bf16 [channels][4];  conv_bias bf16 [channels] or NULL
+ *   conv_state   bf16 [num_conv_slots][3][channels], in place
+ *   g, beta      fp32 [batch][num_v_heads]
+ *   state        fp32 [num_slots][num_v_heads][head_v_dim][head_k_dim], in place
+ *   o            bf16, row b head h at o + b*o_stride + h*head_v_dim
+ *   y            bf16 [batch][y_stride] or NULL
+ *
+ * Errors: GDN_ERR_INVALID (required pointer NULL, negative batch, slot
+ * counts < 1, num_v_heads % num_k_heads, strides too small, o or y
+ * overlapping x, y overlapping o); GDN_ERR_UNSUPPORTED (head dims as for
+ * gdn_fused_recurrent_decode, more than 8192 conv channels read by one q/k
+ * head group, alignment contract); GDN_ERR_HIP.
+ */
+int gdn_fused_conv_decode(const gdn_bf16 *x, int64_t x_stride,
+                          const gdn_bf16 *conv_weight, const gdn_bf16 *conv_bias,
+                          gdn_bf16 *conv_state, int32_t num_conv_slots,
+                          const float *g, const float *beta,
+                          float *state, int32_t num_slots,
+                          const int32_t *state_indices,
+                          gdn_bf16 *o, int64_t o_stride,
+                          gdn_bf16 *y, int64_t y_stride,
+                          int32_t batch, int32_t num_k_heads, int32_t num_v_heads,
+                          int32_t head_k_dim, int32_t head_v_dim, int32_t silu,
+                          float scale, int32_t qk_l2norm, void *stream);
 
 #ifdef __cplusplus
 }

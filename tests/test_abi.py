@@ -182,3 +182,24 @@ def test_chunk_workspace_size_formula():
     for S, T, HK, HV in ((3, 2019, 16, 32), (1, 1, 1, 1), (2, 2048, 16, 32), (0, 0, 16, 32)):
         mc = (T + 63) // 64 + S
         assert gdn.gdn_chunk_workspace_size(S, T, HK, HV) == mc * (HV * (4 * 8192 + 5 * 256) + HK * 16384)
+
+
+def fused(**kw):
+    a = dict(x=X, xs=8192, w=W, b=B, cs=CS, cslots=64, g=G, be=BE, st=ST, slots=64, idx=IDX, o=O, os=4096,
+             y=None, ys=0, B=32, HK=16, HV=32, dk=128, dv=128, silu=1, scale=1.0, norm=1)
+    a.update(kw)
+    return gdn.lib.gdn_fused_conv_decode(a["x"], a["xs"], a["w"], a["b"], a["cs"], a["cslots"], a["g"], a["be"],
+                                         a["st"], a["slots"], a["idx"], a["o"], a["os"], a["y"], a["ys"], a["B"],
+                                         a["HK"], a["HV"], a["dk"], a["dv"], a["silu"], a["scale"], a["norm"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), INV), (dict(w=None), INV), (dict(cs=None), INV), (dict(g=None), INV), (dict(st=None), INV),
+    (dict(idx=None), INV), (dict(o=None), INV), (dict(B=-1), INV), (dict(cslots=0), INV), (dict(slots=0), INV),
+    (dict(HV=24), INV), (dict(xs=8000), INV), (dict(os=1000), INV), (dict(o=X), INV),
+    (dict(y=Y, ys=100), INV), (dict(y=X, ys=8192), INV),
+    (dict(dk=96), UNS), (dict(dv=12), UNS), (dict(xs=8196), UNS), (dict(x=X + 4), UNS), (dict(y=Y + 2, ys=8192), UNS),
+    (dict(HK=1, HV=64, dk=128, dv=128, xs=8448), UNS),   # one q/k group reads > 8192 channels
+])
+def test_fused_validation(kw, code):
+    assert fused(**kw) == code, gdn.lib.gdn_last_error()
