@@ -338,8 +338,11 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
 // ---------------------------------------------------------------------------
 // Only data that crosses waves lives in LDS (the state entering the chunk
 // and R, U, U'); every MFMA operand a wave owns (its K / Q / T / P rows, its
-// K^T rows) is loaded straight from global memory / L2 into registers one
-// phase ahead of use.  45 KB of LDS lets three workgroups share a CU.
+// K^T rows) is loaded straight from global memory / L2 into registers a
+// chunk ahead of use, into the second of two register sets.  45 KB of LDS
+// would let three workgroups share a CU; registers are capped at 256 per
+// lane (two waves per SIMD), so two do, which keeps a 3-sequence prefill
+// (384 workgroups) resident at once.
 struct ScanSmem {
     __bf16 Shi[DVB][LDK], Slo[DVB][LDK];     // S0 [r][d]
     __bf16 Rhi[DVB][LDT], Rlo[DVB][LDT];     // R^T [r][t]
@@ -360,7 +363,7 @@ __device__ __forceinline__ bf16x8 maskf(bool keep, const bf16x8 &v) {
     return __builtin_bit_cast(bf16x8, mask4(keep, __builtin_bit_cast(uint4, v)));
 }
 
-__global__ __launch_bounds__(NTH) void chunk_scan_kernel(RecurrentArgs a, const ChunkRec *recs, const KtRec *kts,
+__global__ __launch_bounds__(NTH, 2) void chunk_scan_kernel(RecurrentArgs a, const ChunkRec *recs, const KtRec *kts,
                                                         int n_vblocks) {
     __shared__ ScanSmem sm;
     const int HV = a.num_v_heads;
@@ -397,67 +400,68 @@ __global__ __launch_bounds__(NTH) void chunk_scan_kernel(RecurrentArgs a, const 
         S[q] = init ? *reinterpret_cast<const f32x4 *>(&S_g[(16 * rt + lr) * DKC + 16 * dt + 4 * lq]) : z;
     }
 
-    // per-lane operands of one chunk; each group is (re)loaded right after
-    // its last use, for the next chunk
-    bf16x8 kf[4], qf[4];                // K, Q rows 16w + lr, dims 32 ks + 8 lq ..
-    f32x4 sb, sbgr, ssqg;               // beta, bgr, sqg of tokens 16w + 4lq + i
-    uint16_t vraw[2][4];                // v of tokens 16w + 4lq + i, rows 16 rt + lr
-    bf16x8 th[2], tl[2];                // T rows 16w + lr, cols 32 ks + 8 lq ..
-    f32x4 su2;                          // u2f of tokens 16w + 4lq + i
-    bf16x8 ph[2], pl[2], ktf[2][2];     // P rows; K^T rows 16 dt + lr
-    float gC;
-
-    auto load_y = [&](int c_t0, int c_n, const ChunkRec *rec) {
+    // per-lane operands of one chunk.  Two register sets alternate (the
+    // chunk loop is unrolled by two), so the next chunk's loads land in the
+    // other set and nothing has to wait for them before the next chunk.
+    struct Ops {
+        bf16x8 kf[4], qf[4];            // K, Q rows 16w + lr, dims 32 ks + 8 lq ..
+        f32x4 sb, sbgr, ssqg, su2;      // factors of tokens 16w + 4lq + i
+        float gc;                       // G_C (stored for every token; a per-lane load)
+        uint16_t vraw[2][4];            // v of tokens 16w + 4lq + i, rows 16 rt + lr
+        bf16x8 th[2], tl[2];            // T rows 16w + lr, cols 32 ks + 8 lq ..
+        bf16x8 ph[2], pl[2];            // P rows 16w + lr
+        bf16x8 ktf[2][2];               // K^T rows 16 (2w + j) + lr
+    };
+    auto load_y = [&](Ops &op, int c_t0, int c_n, const ChunkRec *rec) {
         const int row = c_t0 + min(16 * w + lr, c_n - 1);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            kf[ks] = gfrag(kbase, a.k_stride, row, 32 * ks, lane);
-            qf[ks] = gfrag(qbase, a.q_stride, row, 32 * ks, lane);
+            op.kf[ks] = gfrag(kbase, a.k_stride, row, 32 * ks, lane);
+            op.qf[ks] = gfrag(qbase, a.q_stride, row, 32 * ks, lane);
         }
         const int t4 = 16 * w + 4 * lq;
-        sb = *reinterpret_cast<const f32x4 *>(&rec->beta[t4]);
-        sbgr = *reinterpret_cast<const f32x4 *>(&rec->bgr[t4]);
-        ssqg = *reinterpret_cast<const f32x4 *>(&rec->sqg[t4]);
+        op.sb = *reinterpret_cast<const f32x4 *>(&rec->beta[t4]);
+        op.sbgr = *reinterpret_cast<const f32x4 *>(&rec->bgr[t4]);
+        op.ssqg = *reinterpret_cast<const f32x4 *>(&rec->sqg[t4]);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                vraw[rt][i] = a.v[(int64_t)(c_t0 + min(t4 + i, c_n - 1)) * a.v_stride + (int64_t)h * a.dv +
-                                  vb * DVB + 16 * rt + lr];
+                op.vraw[rt][i] = a.v[(int64_t)(c_t0 + min(t4 + i, c_n - 1)) * a.v_stride + (int64_t)h * a.dv +
+                                     vb * DVB + 16 * rt + lr];
     };
-    auto load_t = [&](const ChunkRec *rec) {
+    auto load_t = [&](Ops &op, const ChunkRec *rec) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            th[ks] = gfrag(&rec->Thi[0][0], CT, 16 * w + lr, 32 * ks, lane);
-            tl[ks] = gfrag(&rec->Tlo[0][0], CT, 16 * w + lr, 32 * ks, lane);
+            op.th[ks] = gfrag(&rec->Thi[0][0], CT, 16 * w + lr, 32 * ks, lane);
+            op.tl[ks] = gfrag(&rec->Tlo[0][0], CT, 16 * w + lr, 32 * ks, lane);
         }
-        su2 = *reinterpret_cast<const f32x4 *>(&rec->u2f[16 * w + 4 * lq]);
+        op.su2 = *reinterpret_cast<const f32x4 *>(&rec->u2f[16 * w + 4 * lq]);
     };
-    auto load_p = [&](const ChunkRec *rec, const KtRec *kt) {
+    auto load_p = [&](Ops &op, const ChunkRec *rec, const KtRec *kt) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            ph[ks] = gfrag(&rec->Phi[0][0], CT, 16 * w + lr, 32 * ks, lane);
-            pl[ks] = gfrag(&rec->Plo[0][0], CT, 16 * w + lr, 32 * ks, lane);
+            op.ph[ks] = gfrag(&rec->Phi[0][0], CT, 16 * w + lr, 32 * ks, lane);
+            op.pl[ks] = gfrag(&rec->Plo[0][0], CT, 16 * w + lr, 32 * ks, lane);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) ktf[j][ks] = gfrag(&kt->Kt[0][0], CT, 16 * (2 * w + j) + lr, 32 * ks, lane);
+            for (int j = 0; j < 2; ++j)
+                op.ktf[j][ks] = gfrag(&kt->Kt[0][0], CT, 16 * (2 * w + j) + lr, 32 * ks, lane);
         }
-        gC = rec->gC[0];
+        op.gc = rec->gC[16 * w + 4 * lq];
     };
 
-    {
-        const ChunkRec *rec = recs + (int64_t)gch * HV + h;
-        const int n0 = min(CT, t_end - t_begin);
-        load_y(t_begin, n0, rec);
-        load_t(rec);
-        load_p(rec, kts + (int64_t)gch * a.num_k_heads + hk);
-    }
-
-    for (int t0 = t_begin; t0 < t_end; t0 += CT, ++gch) {
+    // one chunk: consumes `cur`, prefetches the next chunk into `nxt`
+    auto chunk = [&](const Ops &cur, Ops &nxt, int t0, int gch_c) {
         const int n = min(CT, t_end - t0);
+        // the next chunk's operands; the last chunk reloads its own (always
+        // in bounds, and the loads stay unconditional: no branch for the
+        // wait-count tracking to merge)
         const bool more = t0 + CT < t_end;
-        const int n_next = more ? min(CT, t_end - t0 - CT) : 1;
-        const ChunkRec *rec_next = recs + (int64_t)(gch + 1) * HV + h;
-        const KtRec *kt_next = kts + (int64_t)(gch + 1) * a.num_k_heads + hk;
+        const int t_next = more ? t0 + CT : t0;
+        const int n_next = min(CT, t_end - t_next);
+        const int g_next = more ? gch_c + 1 : gch_c;
+        const ChunkRec *rec_next = recs + (int64_t)g_next * HV + h;
+        const KtRec *kt_next = kts + (int64_t)g_next * a.num_k_heads + hk;
 
         // ---- the state entering the chunk -> LDS (hi/lo)
 #pragma unroll
@@ -469,131 +473,117 @@ __global__ __launch_bounds__(NTH) void chunk_scan_kernel(RecurrentArgs a, const 
             st4(&sm.Slo[16 * rt + lr][16 * dt + 4 * lq], lo);
         }
         __syncthreads();
+        load_y(nxt, t_next, n_next, rec_next);     // next chunk's K, Q, v, factors
 
         // ---- R = b v - bgr (K S0^T) -> LDS;  o part = sqg (Q S0^T)
         const bool live = 16 * w + lr < n;
         f32x4 O[2];
-        {
-            bf16x8 ka[4], qa[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                ka[ks] = maskf(live, kf[ks]);
-                qa[ks] = maskf(live, qf[ks]);
+        for (int rt = 0; rt < 2; ++rt) {
+            f32x4 yk = {0.f, 0.f, 0.f, 0.f}, yq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < DKC / 32; ++ks) {
+                const bf16x8 bh = frag(&sm.Shi[0][0], LDK, 16 * rt, 32 * ks, lane);
+                const bf16x8 bl = frag(&sm.Slo[0][0], LDK, 16 * rt, 32 * ks, lane);
+                const bf16x8 ka = maskf(live, cur.kf[ks]), qa = maskf(live, cur.qf[ks]);
+                yk = mma(ka, bh, yk);
+                yq = mma(qa, bh, yq);
+                yk = mma(ka, bl, yk);
+                yq = mma(qa, bl, yq);
             }
-            float vv[2][4];
+            f32x4 r;
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) vv[rt][i] = 16 * w + 4 * lq + i < n ? bf16_to_f32(vraw[rt][i]) : 0.f;
-            const f32x4 b = sb, bgr = sbgr, sqg = ssqg;
-            if (more) load_y(t0 + CT, n_next, rec_next);     // next chunk's K, Q, v, factors
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                f32x4 yk = {0.f, 0.f, 0.f, 0.f}, yq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < DKC / 32; ++ks) {
-                    const bf16x8 bh = frag(&sm.Shi[0][0], LDK, 16 * rt, 32 * ks, lane);
-                    const bf16x8 bl = frag(&sm.Slo[0][0], LDK, 16 * rt, 32 * ks, lane);
-                    yk = mma(ka[ks], bh, yk);
-                    yq = mma(qa[ks], bh, yq);
-                    yk = mma(ka[ks], bl, yk);
-                    yq = mma(qa[ks], bl, yq);
-                }
-                f32x4 r;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    r[i] = b[i] * vv[rt][i] - bgr[i] * yk[i];
-                    O[rt][i] = sqg[i] * yq[i];
-                }
-                bf16x4 hi, lo;
-                split4(r, hi, lo);
-                st4(&sm.Rhi[16 * rt + lr][16 * w + 4 * lq], hi);
-                st4(&sm.Rlo[16 * rt + lr][16 * w + 4 * lq], lo);
+            for (int i = 0; i < 4; ++i) {
+                const float vv = 16 * w + 4 * lq + i < n ? bf16_to_f32(cur.vraw[rt][i]) : 0.f;
+                r[i] = cur.sb[i] * vv - cur.sbgr[i] * yk[i];
+                O[rt][i] = cur.ssqg[i] * yq[i];
             }
+            bf16x4 hi, lo;
+            split4(r, hi, lo);
+            st4(&sm.Rhi[16 * rt + lr][16 * w + 4 * lq], hi);
+            st4(&sm.Rlo[16 * rt + lr][16 * w + 4 * lq], lo);
         }
         __syncthreads();
+        load_t(nxt, rec_next);
 
         // ---- U = T R (token tile w; T lower triangular) -> LDS, with U' = u2f U
-        {
-            const bf16x8 t_h0 = th[0], t_h1 = th[1], t_l0 = tl[0], t_l1 = tl[1];
-            const f32x4 u2f = su2;
-            if (more) load_t(rec_next);
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (ks > (w >> 1)) break;
-                    const bf16x8 bh = frag(&sm.Rhi[0][0], LDT, 16 * rt, 32 * ks, lane);
-                    const bf16x8 bl = frag(&sm.Rlo[0][0], LDT, 16 * rt, 32 * ks, lane);
-                    const bf16x8 ah = ks ? t_h1 : t_h0, al = ks ? t_l1 : t_l0;
-                    u = mma(ah, bh, u);
-                    u = mma(ah, bl, u);
-                    u = mma(al, bh, u);
-                }
-                f32x4 u2;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) u2[i] = u2f[i] * u[i];
-                bf16x4 hi, lo;
-                split4(u, hi, lo);
-                st4(&sm.Uhi[16 * rt + lr][16 * w + 4 * lq], hi);
-                st4(&sm.Ulo[16 * rt + lr][16 * w + 4 * lq], lo);
-                split4(u2, hi, lo);
-                st4(&sm.U2hi[16 * rt + lr][16 * w + 4 * lq], hi);
-                st4(&sm.U2lo[16 * rt + lr][16 * w + 4 * lq], lo);
-            }
-        }
-        __syncthreads();
-
-        // ---- o = part + P U -> output;  S^T = G_C S^T + K^T U'
-        {
-            bf16x8 p_h[2], p_l[2], kt_f[2][2];
+        for (int rt = 0; rt < 2; ++rt) {
+            f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                p_h[ks] = ph[ks];
-                p_l[ks] = pl[ks];
-                kt_f[0][ks] = ktf[0][ks];
-                kt_f[1][ks] = ktf[1][ks];
+                if (ks > (w >> 1)) break;
+                const bf16x8 bh = frag(&sm.Rhi[0][0], LDT, 16 * rt, 32 * ks, lane);
+                const bf16x8 bl = frag(&sm.Rlo[0][0], LDT, 16 * rt, 32 * ks, lane);
+                u = mma(cur.th[ks], bh, u);
+                u = mma(cur.th[ks], bl, u);
+                u = mma(cur.tl[ks], bh, u);
             }
-            const float g_c = gC;
-            if (more) load_p(rec_next, kt_next);
+            f32x4 u2;
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                f32x4 acc = O[rt];
+            for (int i = 0; i < 4; ++i) u2[i] = cur.su2[i] * u[i];
+            bf16x4 hi, lo;
+            split4(u, hi, lo);
+            st4(&sm.Uhi[16 * rt + lr][16 * w + 4 * lq], hi);
+            st4(&sm.Ulo[16 * rt + lr][16 * w + 4 * lq], lo);
+            split4(u2, hi, lo);
+            st4(&sm.U2hi[16 * rt + lr][16 * w + 4 * lq], hi);
+            st4(&sm.U2lo[16 * rt + lr][16 * w + 4 * lq], lo);
+        }
+        __syncthreads();
+        load_p(nxt, rec_next, kt_next);
+
+        // ---- o = part + P U -> output;  S^T = G_C S^T + K^T U'
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (ks > (w >> 1)) break;
-                    const bf16x8 bh = frag(&sm.Uhi[0][0], LDT, 16 * rt, 32 * ks, lane);
-                    const bf16x8 bl = frag(&sm.Ulo[0][0], LDT, 16 * rt, 32 * ks, lane);
-                    acc = mma(p_h[ks], bh, acc);
-                    acc = mma(p_h[ks], bl, acc);
-                    acc = mma(p_l[ks], bh, acc);
-                }
+        for (int rt = 0; rt < 2; ++rt) {
+            f32x4 acc = O[rt];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * w + 4 * lq + i;
-                    if (t < n)
-                        a.o[(int64_t)(t0 + t) * a.o_stride + (int64_t)h * a.dv + vb * DVB + 16 * rt + lr] =
-                            f32_to_bf16(acc[i]);
-                }
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks > (w >> 1)) break;
+                const bf16x8 bh = frag(&sm.Uhi[0][0], LDT, 16 * rt, 32 * ks, lane);
+                const bf16x8 bl = frag(&sm.Ulo[0][0], LDT, 16 * rt, 32 * ks, lane);
+                acc = mma(cur.ph[ks], bh, acc);
+                acc = mma(cur.ph[ks], bl, acc);
+                acc = mma(cur.pl[ks], bh, acc);
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int rt = q >> 1, j = q & 1;
-                f32x4 acc = S[q] * g_c;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8 bh = frag(&sm.U2hi[0][0], LDT, 16 * rt, 32 * ks, lane);
-                    const bf16x8 bl = frag(&sm.U2lo[0][0], LDT, 16 * rt, 32 * ks, lane);
-                    acc = mma(kt_f[j][ks], bh, acc);
-                    acc = mma(kt_f[j][ks], bl, acc);
-                }
-                S[q] = acc;
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * w + 4 * lq + i;
+                if (t < n)
+                    a.o[(int64_t)(t0 + t) * a.o_stride + (int64_t)h * a.dv + vb * DVB + 16 * rt + lr] =
+                        f32_to_bf16(acc[i]);
             }
+        }
+        const float g_c = cur.gc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int rt = q >> 1, j = q & 1;
+            f32x4 acc = S[q] * g_c;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8 bh = frag(&sm.U2hi[0][0], LDT, 16 * rt, 32 * ks, lane);
+                const bf16x8 bl = frag(&sm.U2lo[0][0], LDT, 16 * rt, 32 * ks, lane);
+                acc = mma(cur.ktf[j][ks], bh, acc);
+                acc = mma(cur.ktf[j][ks], bl, acc);
+            }
+            S[q] = acc;
         }
         // no barrier: the next chunk writes S (read only before the second
         // barrier above), then R, U, U' only after barriers every wave passes
         // once it is done with this chunk
+    };
+
+    Ops A, B;
+    {
+        const ChunkRec *rec = recs + (int64_t)gch * HV + h;
+        load_y(A, t_begin, min(CT, t_end - t_begin), rec);
+        load_t(A, rec);
+        load_p(A, rec, kts + (int64_t)gch * a.num_k_heads + hk);
+    }
+    for (int t0 = t_begin; t0 < t_end; t0 += 2 * CT, gch += 2) {
+        chunk(A, B, t0, gch);
+        if (t0 + CT >= t_end) break;
+        chunk(B, A, t0 + CT, gch + 1);
     }
 
 #pragma unroll
