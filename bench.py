@@ -19,8 +19,10 @@ timed region; every call goes through the C ABI on torch's current stream.
 
 Output: one JSON line.  ``value`` is GDN-layer tokens per second (tokens x
 layers / wall time).  ``roofline`` is for the kernel with the largest share
-of GPU time, timed with HIP events around each of its launches inside the
-timed region.  ``cpu_baseline`` is the fp64 oracle timed on this host on a
+of GPU time; its average launch duration comes from HIP events recorded on
+the launch stream inside the timed region, one pair around each run of
+consecutive launches of that kernel (pre-created, so recording them costs the
+launch stream almost nothing).  ``cpu_baseline`` is the fp64 oracle timed on this host on a
 bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -53,7 +55,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample-requests", type=int, default=8)
+    ap.add_argument("--cpu-sample-requests", type=int, default=14)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -252,8 +254,14 @@ def main():
     n_out = ctypes.c_int32()
 
     def run_pass(timing=None):
-        """One pass of the whole trace through every layer.  ``timing`` maps a
-        kernel kind to a list that receives (start, end) event pairs."""
+        """One pass of the whole trace through every layer.
+
+        ``timing`` (optional) is ``(brackets, events)``: ``brackets`` maps a
+        (step, call) position to "open", "close" or "both", and an event from
+        the pre-created list ``events`` is recorded on the launch stream
+        before an opening and after a closing launch."""
+        brackets, events = timing if timing is not None else ({}, None)
+        ev = 0
         for si, calls in enumerate(plans):
             if n_chunks[si]:
                 # the step's chunk descriptors: built once on the host, uploaded once
@@ -265,18 +273,40 @@ def main():
                     raise RuntimeError("gdn_build_conv_chunks: " + lib.gdn_last_error().decode())
                 ch_dev[2 * a:2 * (a + n_chunks[si])].copy_(ch_host[2 * a:2 * (a + n_chunks[si])],
                                                             non_blocking=True)
-            for kind, fn, fargs, _nb, _nf in calls:
-                rec = timing.get(kind) if timing is not None else None
-                if rec is not None:
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
+            for ci, (kind, fn, fargs, _nb, _nf) in enumerate(calls):
+                br = brackets.get((si, ci))
+                if br in ("open", "both"):
+                    events[ev].record(stream)
+                    ev += 1
                 rc = fn(*fargs)
                 if rc != 0:
                     raise RuntimeError("%s: %s" % (kind, lib.gdn_last_error().decode()))
-                if rec is not None:
-                    e1.record(stream)
-                    rec.append((e0, e1))
+                if br in ("close", "both"):
+                    events[ev].record(stream)
+                    ev += 1
+        return ev
+
+    def bracket_runs(kind):
+        """Event positions that bracket every maximal run of consecutive
+        ``kind`` launches (in launch order), and the number of events.  Kernels
+        on one stream run back to back, so a run's span is the sum of its
+        kernels' durations plus the (sub-microsecond) dispatch gaps between
+        them; an event pair per launch instead would stall the host-side
+        launch stream and add idle gaps to the timed region."""
+        order = [(si, ci, c[0]) for si, calls in enumerate(plans) for ci, c in enumerate(calls)]
+        br, n_ev = {}, 0
+        for j, (si, ci, k) in enumerate(order):
+            if k != kind:
+                continue
+            first = j == 0 or order[j - 1][2] != kind
+            last = j == len(order) - 1 or order[j + 1][2] != kind
+            if first or last:
+                br[(si, ci)] = "both" if first and last else ("open" if first else "close")
+                n_ev += 2 if first and last else 1
+        return br, n_ev
+
+    def span_ms(events, n_ev):
+        return sum(events[i].elapsed_time(events[i + 1]) for i in range(0, n_ev, 2))
 
     def totals(kind):
         nb = sum(c[3] for calls in plans for c in calls if c[0] == kind)
@@ -290,12 +320,13 @@ def main():
     for _ in range(args.warmup):
         run_pass()
     torch.cuda.synchronize()
-    prof = {k: [] for k in kinds}
-    run_pass(prof)
-    torch.cuda.synchronize()
     kern = {}
     for k in kinds:
-        ms = sum(e0.elapsed_time(e1) for e0, e1 in prof[k])
+        br, n_ev = bracket_runs(k)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        run_pass((br, evs))
+        torch.cuda.synchronize()
+        ms = span_ms(evs, n_ev)
         n, nb, nf = totals(k)
         kern[k] = {"launches_per_step": n, "ms_per_step": ms, "avg_us": 1e3 * ms / max(n, 1),
                    "gb_per_s": nb / (ms * 1e-3) / 1e9 if ms else 0.0,
@@ -304,16 +335,17 @@ def main():
             kern[k]["tflop_per_s"] = nf / (ms * 1e-3) / 1e12
     dominant = max(kinds, key=lambda k: kern[k]["ms_per_step"])
 
-    # ---- timed region
+    # ---- timed region: the dominant kernel's runs bracketed by pre-created events
+    br, n_ev = bracket_runs(dominant)
+    live = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    live = {dominant: []}
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run_pass(live)
+    for i in range(args.steps):
+        run_pass((br, live[i]))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    ms_dom = sum(e0.elapsed_time(e1) for e0, e1 in live[dominant]) / args.steps
+    ms_dom = sum(span_ms(evs, n_ev) for evs in live) / args.steps
     n, nb, nf = totals(dominant)
     avg_us = 1e3 * ms_dom / n
     if dominant == "recurrent_chunk":
@@ -322,12 +354,12 @@ def main():
         achieved = nf / (ms_dom * 1e-3) / 1e12
         roof = {"kernel": dominant, "bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
-                "avg_launch_us": avg_us, "algorithmic_per_launch": nf / n}
+                "avg_launch_us": avg_us, "algorithmic_per_launch": nf / n, "timed_runs_per_step": n_ev // 2}
     else:
         achieved = nb / (ms_dom * 1e-3) / 1e9
         roof = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                "avg_launch_us": avg_us, "algorithmic_per_launch": nb / n}
+                "avg_launch_us": avg_us, "algorithmic_per_launch": nb / n, "timed_runs_per_step": n_ev // 2}
 
     ms_per_step = 1e3 * wall / args.steps
     value = T_all * L * args.steps / wall
