@@ -45,7 +45,6 @@ constexpr int LDT = CT + 8;     // padded LDS row (bf16) of a [*][64] tile
 constexpr int LDF = CT + 4;     // padded LDS row (fp32) of a [64][64] tile
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // workspace records
@@ -101,6 +100,16 @@ __device__ __forceinline__ void split4(const f32x4 &v, bf16x4 &hi, bf16x4 &lo) {
 }
 
 __device__ __forceinline__ void st4(__bf16 *p, const bf16x4 &v) { *reinterpret_cast<bf16x4 *>(p) = v; }
+
+// Workspace and final-state stores are streaming (nontemporal): each element
+// is written once per launch, so no dirty lines of this launch are left in
+// the caches for the next kernel to write back.
+__device__ __forceinline__ void st4_stream(__bf16 *p, const bf16x4 &v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<bf16x4 *>(p));
+}
+__device__ __forceinline__ void st8_stream(__bf16 *p, const bf16x8 &v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<bf16x8 *>(p));
+}
 
 // C += X Y for 16x16 fp32 tiles in LDS; four 16x16x4 fp32 MFMAs
 __device__ __forceinline__ f32x4 mm16_f32(const float (*X)[LDF], int xr, int xc, const float (*Y)[LDF], int yr,
@@ -231,9 +240,9 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
         bf16x8 col[4];
 #pragma unroll
         for (int j = 0; j < 32; ++j) col[j >> 3][j & 7] = sm.K[32 * half + j][d];
-        uint4 *dst = reinterpret_cast<uint4 *>(&kts[(int64_t)gch * a.num_k_heads + hk].Kt[d][32 * half]);
+        __bf16 *dst = &kts[(int64_t)gch * a.num_k_heads + hk].Kt[d][32 * half];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) dst[m] = __builtin_bit_cast(uint4, col[m]);
+        for (int m = 0; m < 4; ++m) st8_stream(dst + 8 * m, col[m]);
     }
 
     // ---- stage 1: tiles (i-tile c, t-tile w) of K K^T and K Q^T, laid out
@@ -247,8 +256,8 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
             const int i0 = 16 * c + 4 * lq;
             if (c > w) {
                 const bf16x4 z = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-                st4(&rec->Phi[t][i0], z);
-                st4(&rec->Plo[t][i0], z);
+                st4_stream(&rec->Phi[t][i0], z);
+                st4_stream(&rec->Plo[t][i0], z);
                 continue;
             }
             f32x4 kk = {0.f, 0.f, 0.f, 0.f}, kq = {0.f, 0.f, 0.f, 0.f};
@@ -271,8 +280,8 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
             *reinterpret_cast<f32x4 *>(&sm.A[t][i0]) = av;
             bf16x4 ph, pl;
             split4(pv, ph, pl);
-            st4(&rec->Phi[t][i0], ph);
-            st4(&rec->Plo[t][i0], pl);
+            st4_stream(&rec->Phi[t][i0], ph);
+            st4_stream(&rec->Plo[t][i0], pl);
         }
     }
     __syncthreads();
@@ -327,8 +336,8 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
                 hv[q] = hi;
                 lv[q] = lo;
             }
-            *reinterpret_cast<bf16x8 *>(&rec->Thi[t][i0]) = hv;
-            *reinterpret_cast<bf16x8 *>(&rec->Tlo[t][i0]) = lv;
+            st8_stream(&rec->Thi[t][i0], hv);
+            st8_stream(&rec->Tlo[t][i0], lv);
         }
     }
 }
@@ -397,7 +406,7 @@ __global__ __launch_bounds__(NTH, 2) void chunk_scan_kernel(RecurrentArgs a, con
     for (int q = 0; q < 4; ++q) {
         const int rt = q >> 1, dt = 2 * w + (q & 1);
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        S[q] = init ? *reinterpret_cast<const f32x4 *>(&S_g[(16 * rt + lr) * DKC + 16 * dt + 4 * lq]) : z;
+        S[q] = init ? load_stream4(&S_g[(16 * rt + lr) * DKC + 16 * dt + 4 * lq]) : z;
     }
 
     // per-lane operands of one chunk.  Two register sets alternate (the
@@ -589,7 +598,7 @@ __global__ __launch_bounds__(NTH, 2) void chunk_scan_kernel(RecurrentArgs a, con
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int rt = q >> 1, dt = 2 * w + (q & 1);
-        *reinterpret_cast<f32x4 *>(&S_g[(16 * rt + lr) * DKC + 16 * dt + 4 * lq]) = S[q];
+        store_stream4(&S_g[(16 * rt + lr) * DKC + 16 * dt + 4 * lq], S[q]);
     }
 }
 

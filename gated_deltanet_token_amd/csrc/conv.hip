@@ -23,15 +23,28 @@ constexpr int kConvThreads = 256;                       // 4 waves
 constexpr int kConvTile = kConvThreads * kConvVec;      // 2048 channels
 constexpr int kChunk = 8;                               // tokens per descriptor
 
-__global__ __launch_bounds__(kConvThreads) void conv_varlen_kernel(
+template <int THREADS, bool SILU>
+__global__ __launch_bounds__(THREADS) void conv_varlen_kernel(
     const uint16_t *__restrict__ x, int64_t x_stride, const uint16_t *__restrict__ weight,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ conv_state,
     const int32_t *__restrict__ qsl, const int32_t *__restrict__ state_indices,
-    const uint8_t *__restrict__ has_init, const gdn_conv_chunk *__restrict__ chunks, int n_chunks,
-    uint16_t *__restrict__ y, int64_t y_stride, int channels, int silu) {
+    const uint8_t *__restrict__ has_init, const gdn_conv_chunk *__restrict__ chunks,
+    uint16_t *__restrict__ y, int64_t y_stride, int channels, int n_tiles) {
+    constexpr int TILE = THREADS * kConvVec;
+    // Chunk-major and XCD-contiguous: each XCD takes one contiguous range of
+    // (descriptor, channel tile) items, so a chunk's halo rows are rows its
+    // neighbouring chunk fetched into the same L2.
     const int work = xcd_contiguous(blockIdx.x, gridDim.x);
-    const int tile = work / n_chunks;
-    const int ci = work - tile * n_chunks;
+    const int ci = work / n_tiles;
+    const int tile = work - ci * n_tiles;
+    const int c0 = tile * TILE + threadIdx.x * kConvVec;
+    if (c0 >= channels) return;
+
+    // The taps first: they do not depend on the descriptor, and the first
+    // output row needs them, so its wait does not cover the row loads.
+    ConvTaps taps;
+    load_taps(taps, weight, bias, c0);
+
     const gdn_conv_chunk d = chunks[ci];
     const int slot = state_indices[d.seq];
     if (slot < 0) return;
@@ -40,43 +53,43 @@ __global__ __launch_bounds__(kConvThreads) void conv_varlen_kernel(
     const int t0 = a + d.chunk * kChunk;
     if (t0 >= end) return;
     const int n = min(kChunk, end - t0);
-    const int c0 = tile * kConvTile + threadIdx.x * kConvVec;
-    if (c0 >= channels) return;
 
     uint16_t *st = conv_state + (int64_t)slot * 3 * channels + c0;
-    const uint4 zero = make_uint4(0, 0, 0, 0);
 
     // window rows: h[0..2] = halo (oldest first), r[0..n) = this chunk's tokens.
     // Every load reads a valid address (halo: the slot or the 3 preceding
     // rows of the same sequence; tokens past the chunk end re-read its last
-    // row) and masking is done on values, so no load is predicated.
+    // row) and masking is done on values, so no load is predicated.  A
+    // sequence without an initial state zeroes its halo through a mask.
     uint4 h[3], r[kChunk];
     const bool first = d.chunk == 0;
-    const bool zero_halo = first && has_init != nullptr && has_init[d.seq] == 0;
     const uint16_t *hp = first ? st : x + (int64_t)(t0 - 3) * x_stride + c0;
     const int64_t hstride = first ? (int64_t)channels : x_stride;
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(hp + i * hstride);
-        h[i] = select4(zero_halo, zero, v);
-    }
+    for (int i = 0; i < 3; ++i) h[i] = *reinterpret_cast<const uint4 *>(hp + i * hstride);
 #pragma unroll
     for (int i = 0; i < kChunk; ++i)
         r[i] = *reinterpret_cast<const uint4 *>(x + (int64_t)(t0 + min(i, n - 1)) * x_stride + c0);
+    // (the flag is read unconditionally, from a valid byte, for the same reason as the bias)
+    const uint8_t flag = *(has_init != nullptr ? has_init + d.seq : reinterpret_cast<const uint8_t *>(chunks + ci));
+    const uint32_t keep = (first && has_init != nullptr && flag == 0) ? 0u : ~0u;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) h[i] = make_uint4(h[i].x & keep, h[i].y & keep, h[i].z & keep, h[i].w & keep);
 
-    ConvTaps taps;
-    load_taps(taps, weight, bias, c0);
-
-    const bool act = silu != 0;
+    // Output rows, streamed out (written once, not read again by this
+    // launch).  Window row j is h[j] for j < 3, else r[j - 3]; pair j holds
+    // window rows (j, j + 1) and serves output rows j and j - 2.
+    RowPairs pr[kChunk + 2];
+#pragma unroll
+    for (int j = 0; j < kChunk + 2; ++j) {
+        const uint4 &older = j < 3 ? h[j] : r[j - 3];
+        const uint4 &newer = j + 1 < 3 ? h[j + 1] : r[j - 2];
+        pr[j] = row_pairs(older, newer);
+    }
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
-        if (i < n) {
-            const uint4 e0 = i >= 3 ? r[i - 3] : h[i];
-            const uint4 e1 = i >= 2 ? r[i - 2] : h[i + 1];
-            const uint4 e2 = i >= 1 ? r[i - 1] : h[2];
-            const uint4 out = conv_row(taps, e0, e1, e2, r[i], act);
-            *reinterpret_cast<uint4 *>(y + (int64_t)(t0 + i) * y_stride + c0) = out;
-        }
+        const uint4 out = conv_pairs(taps, pr[i], pr[i + 2], SILU);
+        if (i < n) store_stream16(y + (int64_t)(t0 + i) * y_stride + c0, out);
     }
 
     if (first) {
@@ -120,15 +133,26 @@ __global__ __launch_bounds__(kConvThreads) void conv_update_kernel(
     *reinterpret_cast<uint4 *>(st + 2 * (int64_t)channels) = xv;
 }
 
-hipError_t launch_conv_varlen(const ConvVarlenArgs &a, hipStream_t stream) {
-    const int n_tiles = (a.channels + kConvTile - 1) / kConvTile;
+template <int THREADS>
+hipError_t launch_conv_varlen_t(const ConvVarlenArgs &a, hipStream_t stream) {
+    constexpr int TILE = THREADS * kConvVec;
+    const int n_tiles = (a.channels + TILE - 1) / TILE;
     const long long blocks = (long long)a.n_chunks * n_tiles;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(conv_varlen_kernel, dim3((unsigned)blocks), dim3(kConvThreads), 0, stream,
-                       a.x, a.x_stride, a.weight, a.bias, a.conv_state, a.qsl, a.state_indices,
-                       a.has_init, a.chunks, a.n_chunks, a.y, a.y_stride, a.channels, a.silu);
+    if (a.silu)
+        hipLaunchKernelGGL((conv_varlen_kernel<THREADS, true>), dim3((unsigned)blocks), dim3(THREADS), 0, stream,
+                           a.x, a.x_stride, a.weight, a.bias, a.conv_state, a.qsl, a.state_indices, a.has_init,
+                           a.chunks, a.y, a.y_stride, a.channels, n_tiles);
+    else
+        hipLaunchKernelGGL((conv_varlen_kernel<THREADS, false>), dim3((unsigned)blocks), dim3(THREADS), 0, stream,
+                           a.x, a.x_stride, a.weight, a.bias, a.conv_state, a.qsl, a.state_indices, a.has_init,
+                           a.chunks, a.y, a.y_stride, a.channels, n_tiles);
     return hipGetLastError();
+}
+
+hipError_t launch_conv_varlen(const ConvVarlenArgs &a, hipStream_t stream) {
+    return launch_conv_varlen_t<kConvThreads>(a, stream);
 }
 
 hipError_t launch_conv_update(const ConvUpdateArgs &a, hipStream_t stream) {

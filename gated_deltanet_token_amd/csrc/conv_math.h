@@ -1,6 +1,14 @@
 // Width-4 causal conv arithmetic shared by the conv kernels and the fused
 // conv + recurrence decode: the same operations in the same order, so every
 // path gives bit-identical conv outputs.
+//
+// Per channel the output is bias + w0 e0 + w1 e1 + w2 e2 + w3 e3 (e0 the
+// oldest window row).  The sum runs on the gfx950 bf16 dot product
+// (v_dot2_f32_bf16: two bf16 products added to an fp32 accumulator): the
+// weights of a channel are already stored as the bf16 pairs (w0, w1) and
+// (w2, w3), and one byte permute pairs a channel's value in two window rows.
+// Products of bf16 values are exact in fp32, so this is the fp32 sum of the
+// same terms, two at a time, without unpacking any operand.
 #pragma once
 
 #include "gdn_device.h"
@@ -10,7 +18,8 @@ namespace gdn {
 constexpr int kConvVec = 8;   // channels per lane (one 16-byte bf16 vector)
 
 struct ConvTaps {
-    float w[kConvVec][4];
+    uint32_t w01[kConvVec];   // bf16 pair (tap 0, tap 1) of each channel
+    uint32_t w23[kConvVec];   // bf16 pair (tap 2, tap 3)
     float b[kConvVec];
 };
 
@@ -21,17 +30,17 @@ __device__ __forceinline__ void load_taps(ConvTaps &t, const uint16_t *weight, c
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint4 v = wp[i];           // channels 2i and 2i+1
-        t.w[2 * i][0] = bf16_lo(v.x);     t.w[2 * i][1] = bf16_hi(v.x);
-        t.w[2 * i][2] = bf16_lo(v.y);     t.w[2 * i][3] = bf16_hi(v.y);
-        t.w[2 * i + 1][0] = bf16_lo(v.z); t.w[2 * i + 1][1] = bf16_hi(v.z);
-        t.w[2 * i + 1][2] = bf16_lo(v.w); t.w[2 * i + 1][3] = bf16_hi(v.w);
+        t.w01[2 * i] = v.x;
+        t.w23[2 * i] = v.y;
+        t.w01[2 * i + 1] = v.z;
+        t.w23[2 * i + 1] = v.w;
     }
-    if (bias) {
-        unpack8(*reinterpret_cast<const uint4 *>(bias + c0), t.b);
-    } else {
-#pragma unroll
-        for (int c = 0; c < kConvVec; ++c) t.b[c] = 0.0f;
-    }
+    // Without a bias the load still reads a valid address (the weights) and
+    // the value is zeroed: a load behind a branch would make the compiler
+    // wait for it, and everything issued before it, at the join.
+    const uint4 bv = *reinterpret_cast<const uint4 *>(bias ? bias + c0 : weight + c0);
+    const uint32_t keep = bias ? ~0u : 0u;
+    unpack8(make_uint4(bv.x & keep, bv.y & keep, bv.z & keep, bv.w & keep), t.b);
 }
 
 __device__ __forceinline__ uint4 select4(bool c, const uint4 &a, const uint4 &b) {
@@ -42,23 +51,54 @@ __device__ __forceinline__ float silu_f32(float z) {
     return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
-// One output row from four window rows (oldest first).  The accumulation
-// order -- bias, then taps 0..3 with fused multiply-adds -- is the same in the
-// varlen and the update kernels, so both give bit-identical results.
-__device__ __forceinline__ uint4 conv_row(const ConvTaps &t, const uint4 &e0, const uint4 &e1,
-                                          const uint4 &e2, const uint4 &e3, bool silu) {
-    float f0[8], f1[8], f2[8], f3[8], out[8];
-    unpack8(e0, f0); unpack8(e1, f1); unpack8(e2, f2); unpack8(e3, f3);
+// bf16 pair (older, newer) of the even / odd channel of two packed words
+__device__ __forceinline__ uint32_t pair_even(uint32_t older, uint32_t newer) {
+    return __builtin_amdgcn_perm(newer, older, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_odd(uint32_t older, uint32_t newer) {
+    return __builtin_amdgcn_perm(newer, older, 0x07060302u);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// The 8 channels of two consecutive window rows as bf16 pairs (older, newer),
+// channel c in p[c].  An output row uses the pairs of its window rows (0, 1)
+// and (2, 3); a kernel that produces several rows builds each pair of
+// neighbouring rows once.
+struct RowPairs {
+    uint32_t p[kConvVec];
+};
+
+__device__ __forceinline__ RowPairs row_pairs(const uint4 &older, const uint4 &newer) {
+    RowPairs r;
+    r.p[0] = pair_even(older.x, newer.x); r.p[1] = pair_odd(older.x, newer.x);
+    r.p[2] = pair_even(older.y, newer.y); r.p[3] = pair_odd(older.y, newer.y);
+    r.p[4] = pair_even(older.z, newer.z); r.p[5] = pair_odd(older.z, newer.z);
+    r.p[6] = pair_even(older.w, newer.w); r.p[7] = pair_odd(older.w, newer.w);
+    return r;
+}
+
+// One output row from the pairs of its window rows (0, 1) and (2, 3).  The
+// accumulation order -- bias, then taps (0, 1), then taps (2, 3) -- is the
+// same in every kernel, so all give bit-identical results.
+__device__ __forceinline__ uint4 conv_pairs(const ConvTaps &t, const RowPairs &p01, const RowPairs &p23,
+                                            bool silu) {
+    float out[kConvVec];
 #pragma unroll
     for (int c = 0; c < kConvVec; ++c) {
-        float acc = t.b[c];
-        acc = __builtin_fmaf(t.w[c][0], f0[c], acc);
-        acc = __builtin_fmaf(t.w[c][1], f1[c], acc);
-        acc = __builtin_fmaf(t.w[c][2], f2[c], acc);
-        acc = __builtin_fmaf(t.w[c][3], f3[c], acc);
+        float acc = dot2_bf16(p01.p[c], t.w01[c], t.b[c]);
+        acc = dot2_bf16(p23.p[c], t.w23[c], acc);
         out[c] = silu ? silu_f32(acc) : acc;
     }
     return pack8(out);
+}
+
+// One output row from four window rows (oldest first).
+__device__ __forceinline__ uint4 conv_row(const ConvTaps &t, const uint4 &e0, const uint4 &e1,
+                                          const uint4 &e2, const uint4 &e3, bool silu) {
+    return conv_pairs(t, row_pairs(e0, e1), row_pairs(e2, e3), silu);
 }
 
 }  // namespace gdn

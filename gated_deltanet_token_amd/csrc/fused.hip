@@ -21,7 +21,11 @@ namespace gdn {
 
 namespace {
 
-constexpr int kFusedThreads = 512;                 // 8 waves
+// 4 waves, 8 state rows per lane group: at the decode shape (2 v heads of
+// 128 rows per q/k head) one pass covers the whole group, and the 512
+// workgroups of a 32-sequence batch are all resident at once on 256 CUs.
+constexpr int kFusedThreads = 256;
+constexpr int kFusedRows = 8;                      // rows per lane group per pass
 constexpr int kMaxGroupChannels = 8192;            // q + k + v channels of one head group
 
 template <int DK, int R>
@@ -32,16 +36,49 @@ __global__ __launch_bounds__(kFusedThreads) void fused_conv_decode_kernel(FusedD
     extern __shared__ uint16_t act[];                         // conv output of this group: q | k | v
 
     const int HK = a.num_k_heads, HV = a.num_v_heads, grp = HV / HK;
-    const int b = blockIdx.x / HK;
-    const int hk = blockIdx.x - b * HK;
+    // XCD-contiguous order: each XCD takes a contiguous range of (sequence, head group)
+    const int bid = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int b = bid / HK;
+    const int hk = bid - b * HK;
     const int slot = a.state_indices[b];
     if (slot < 0) return;
     const int tid = threadIdx.x;
     const int dv = a.dv;
     const int nq = DK, nv = grp * dv;                         // channels: q and k DK each, v grp*dv
     const int n_vec = (2 * nq + nv) / kConvVec;
+    const int j = (tid & 63) % G;
+    const int n_rows = nv;
 
-    // ---- conv update of the group's channels
+    // one pass of state rows: row r of this lane group, loaded as streaming
+    // 16-byte vectors (each state element is read and written once)
+    int row[R];
+    bool valid[R];
+    float S[R][E];
+    auto load_rows = [&](int base) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            row[r] = base + r * ROWS_PER_PASS + tid / G;      // row within the group
+            valid[r] = row[r] < n_rows;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int h = hk * grp + row[r] / dv, i = row[r] % dv;
+            const float *Sp = a.state + (((int64_t)slot * HV + h) * dv + i) * DK + 4 * j;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                f32x4 v4 = {0.f, 0.f, 0.f, 0.f};
+                if (valid[r]) v4 = load_stream4(Sp + 4 * G * m);
+                S[r][4 * m + 0] = v4.x;
+                S[r][4 * m + 1] = v4.y;
+                S[r][4 * m + 2] = v4.z;
+                S[r][4 * m + 3] = v4.w;
+            }
+        }
+    };
+
+    // ---- conv update of the group's channels.  The first pass of state
+    // loads is issued right after the conv loads: it does not depend on the
+    // conv, so its latency overlaps the conv arithmetic and the barrier.
     for (int c = tid; c < n_vec; c += kFusedThreads) {
         const int lc = c * kConvVec;                          // channel within the group (q | k | v)
         int ch;                                               // channel within the conv row
@@ -55,6 +92,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_conv_decode_kernel(FusedD
         const uint4 xv = *reinterpret_cast<const uint4 *>(a.x + (int64_t)b * a.x_stride + ch);
         ConvTaps taps;
         load_taps(taps, a.conv_weight, a.conv_bias, ch);
+        if (c == tid) load_rows(0);
         const uint4 out = conv_row(taps, s0, s1, s2, xv, a.silu != 0);
         *reinterpret_cast<uint4 *>(st) = s1;
         *reinterpret_cast<uint4 *>(st + a.channels) = s2;
@@ -62,11 +100,10 @@ __global__ __launch_bounds__(kFusedThreads) void fused_conv_decode_kernel(FusedD
         if (a.y) *reinterpret_cast<uint4 *>(a.y + (int64_t)b * a.y_stride + ch) = out;
         *reinterpret_cast<uint4 *>(&act[lc]) = out;
     }
+    if (tid >= n_vec) load_rows(0);
     __syncthreads();
 
     // ---- gated delta rule, one token, for the grp * dv rows of the group
-    const int lane = tid & 63;
-    const int j = lane % G;
     float kf[E], qf[E];
 #pragma unroll
     for (int m = 0; m < M; ++m)
@@ -77,45 +114,24 @@ __global__ __launch_bounds__(kFusedThreads) void fused_conv_decode_kernel(FusedD
         }
     const TokenFactors f = token_factors<G, E>(kf, qf, a.l2norm != 0);
 
-    const int n_rows = nv;
     for (int base = 0; base < n_rows; base += R * ROWS_PER_PASS) {
-        int row[R];
-        bool valid[R];
-        float S[R][E];
+        if (base > 0) load_rows(base);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            row[r] = base + r * ROWS_PER_PASS + tid / G;          // row within the group
-            valid[r] = row[r] < n_rows;
-        }
-        // issue every row's loads before any arithmetic
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int h = hk * grp + row[r] / dv, i = row[r] % dv;
-            const float *Sp = a.state + (((int64_t)slot * HV + h) * dv + i) * DK + 4 * j;
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (valid[r]) v4 = *reinterpret_cast<const float4 *>(Sp + 4 * G * m);
-                S[r][4 * m + 0] = v4.x;
-                S[r][4 * m + 1] = v4.y;
-                S[r][4 * m + 2] = v4.z;
-                S[r][4 * m + 3] = v4.w;
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int h = hk * grp + min(row[r], n_rows - 1) / dv, i = min(row[r], n_rows - 1) % dv;
+            const int rr = min(row[r], n_rows - 1);
+            const int h = hk * grp + rr / dv, i = rr % dv;
             const float alpha = expf(a.g[(int64_t)b * HV + h]);
             const float beta = a.beta[(int64_t)b * HV + h];
-            const float v = bf16_to_f32(act[2 * nq + min(row[r], n_rows - 1)]);
+            const float v = bf16_to_f32(act[2 * nq + rr]);
             const float out = row_step<G, E>(S[r], kf, qf, f, alpha, beta, v, a.scale);
             if (valid[r]) {
                 if (j == 0) a.o[(int64_t)b * a.o_stride + (int64_t)h * dv + i] = f32_to_bf16(out);
                 float *Sp = a.state + (((int64_t)slot * HV + h) * dv + i) * DK + 4 * j;
 #pragma unroll
-                for (int m = 0; m < M; ++m)
-                    *reinterpret_cast<float4 *>(Sp + 4 * G * m) =
-                        make_float4(S[r][4 * m + 0], S[r][4 * m + 1], S[r][4 * m + 2], S[r][4 * m + 3]);
+                for (int m = 0; m < M; ++m) {
+                    const f32x4 w = {S[r][4 * m + 0], S[r][4 * m + 1], S[r][4 * m + 2], S[r][4 * m + 3]};
+                    store_stream4(Sp + 4 * G * m, w);
+                }
             }
         }
     }
@@ -128,7 +144,7 @@ hipError_t launch_dk(const FusedDecodeArgs &a, hipStream_t stream) {
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const int grp = a.num_v_heads / a.num_k_heads;
     const size_t lds = (size_t)(2 * DK + grp * a.dv) * sizeof(uint16_t);
-    hipLaunchKernelGGL((fused_conv_decode_kernel<DK, 4>), dim3((unsigned)blocks), dim3(kFusedThreads), lds, stream,
+    hipLaunchKernelGGL((fused_conv_decode_kernel<DK, kFusedRows>), dim3((unsigned)blocks), dim3(kFusedThreads), lds, stream,
                        a);
     return hipGetLastError();
 }

@@ -28,6 +28,28 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
 }
 
+// ---------------------------------------------------------------------------
+// Streaming 16-byte fp32 access (nontemporal hint) for data that a launch
+// reads once and writes once, such as the recurrent state: it is not kept in
+// the caches for reuse that never comes.
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 load_stream4(const float *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+}
+__device__ __forceinline__ void store_stream4(float *p, f32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
+}
+
+// streaming 16-byte store of 8 bf16 (an output row slice written once)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store_stream16(uint16_t *p, const uint4 &v) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
+}
+
 // unpack 8 bf16 (one 16-byte vector) into fp32
 __device__ __forceinline__ void unpack8(const uint4 &v, float *f) {
     f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);

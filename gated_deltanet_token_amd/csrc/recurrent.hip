@@ -15,7 +15,8 @@
 // {32m + 4j + e | e < 4} for dk = 128 (float4 slices m = 0..3), so every
 // load/store instruction of a wave moves whole 128-byte lines of 8
 // neighbouring rows.  The state stays in VGPRs for the whole token loop and
-// is read and written exactly once per call.
+// is read and written exactly once per call, with streaming (nontemporal)
+// 16-byte accesses.
 //
 // Per token (gdr_math.h), with raw (unnormalised) q and k and rk, rq the
 // inverse norms:
@@ -87,9 +88,8 @@ __global__ __launch_bounds__(64 * W) void recurrent_kernel(RecurrentArgs a, int 
     for (int r = 0; r < R; ++r) {
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (init && valid[r])
-                v4 = *reinterpret_cast<const float4 *>(S_head + (int64_t)row[r] * DK + m * 4 * G + 4 * j);
+            f32x4 v4 = {0.f, 0.f, 0.f, 0.f};
+            if (init && valid[r]) v4 = load_stream4(S_head + (int64_t)row[r] * DK + m * 4 * G + 4 * j);
             S[r][4 * m + 0] = v4.x;
             S[r][4 * m + 1] = v4.y;
             S[r][4 * m + 2] = v4.z;
@@ -160,8 +160,8 @@ __global__ __launch_bounds__(64 * W) void recurrent_kernel(RecurrentArgs a, int 
         if (!valid[r]) continue;
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            float4 v4 = make_float4(S[r][4 * m + 0], S[r][4 * m + 1], S[r][4 * m + 2], S[r][4 * m + 3]);
-            *reinterpret_cast<float4 *>(S_head + (int64_t)row[r] * DK + m * 4 * G + 4 * j) = v4;
+            const f32x4 v4 = {S[r][4 * m + 0], S[r][4 * m + 1], S[r][4 * m + 2], S[r][4 * m + 3]};
+            store_stream4(S_head + (int64_t)row[r] * DK + m * 4 * G + 4 * j, v4);
         }
     }
 }
@@ -180,10 +180,12 @@ static hipError_t launch_shape(const RecurrentArgs &a, hipStream_t stream) {
 
 template <int DK>
 static hipError_t launch_dk(const RecurrentArgs &a, hipStream_t stream) {
-    // decode (one token per sequence): 4 waves x 8 rows per workgroup;
-    // varlen: the same shape for now.  Per-row arithmetic is shape-independent.
-    if (a.qsl == nullptr) return launch_shape<DK, 4, 1, false>(a, stream);
-    return launch_shape<DK, 4, 1, true>(a, stream);
+    // 2 waves x 8 rows per workgroup (dk >= 32): the fastest of the shapes
+    // measured at the 32-sequence decode (many small workgroups keep more
+    // state loads in flight than fewer large ones).  Per-row arithmetic is
+    // shape-independent, so decode and varlen give identical tokens.
+    if (a.qsl == nullptr) return launch_shape<DK, 2, 1, false>(a, stream);
+    return launch_shape<DK, 2, 1, true>(a, stream);
 }
 
 hipError_t launch_recurrent(const RecurrentArgs &a, hipStream_t stream) {
