@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample-requests", type=int, default=14)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-isolated", action="store_true",
+                    help="skip the per-call measurements at the c32 shapes with HBM-only operands")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit: the "
@@ -100,6 +102,181 @@ def flops_recurrent(tokens):
 
 
 # ---------------------------------------------------------------------------
+# memory traffic per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+# ---------------------------------------------------------------------------
+# The counter figures live in a committed profile summary, one "traffic-record"
+# line per kernel, together with a digest of the kernel's source files at the
+# time the counters were taken.  A figure is used only while the sources still
+# match: after any change to the kernel it is reported as null until measured
+# again.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c32_trace_4layers.md")
+_CSRC = os.path.join(ROOT, "gated_deltanet_token_amd", "csrc")
+KERNEL_SOURCES = {
+    "fused_decode": ["fused.hip", "conv_math.h", "gdr_math.h", "gdn_device.h", "gdn_internal.h"],
+    "conv_varlen": ["conv.hip", "conv_math.h", "gdn_device.h", "gdn_internal.h"],
+    "recurrent_chunk": ["chunk.hip", "gdn_device.h", "gdn_internal.h"],
+}
+
+
+def sources_digest(kind):
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(_CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read() + b"\0")
+    return h.hexdigest()[:16]
+
+
+def traffic_per_launch(kind):
+    """Measured HBM bytes (fetch + write) per launch of ``kind`` in the trace,
+    or None if there is no record for the current sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = [ln.split() for ln in f if ln.startswith("traffic-record ")]
+    except OSError:
+        return None
+    for parts in lines:
+        rec = dict(p.split("=", 1) for p in parts[1:])
+        if rec.get("kernel") == kind and rec.get("sources") == sources_digest(kind):
+            return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
+    return None
+
+
+# ---------------------------------------------------------------------------
+# every call of the path alone at its c32 shape, from HBM
+# ---------------------------------------------------------------------------
+
+def isolated(seed, reps=64):
+    """Each hot-path call alone at its c32 shape with its operands in HBM.
+
+    The operands rotate over buffer sets that together exceed the 256 MB
+    Infinity Cache several times, so no launch finds its inputs in a cache.
+    A sleep kernel at the head of the stream lets the host queue every timed
+    launch before the first one starts, so host-side launch cost does not
+    open gaps between kernels.  Returns {call: {...}} with the average launch
+    time from HIP events on the launch stream."""
+    import torch
+    import gated_deltanet_token_amd as gdn
+    import synth
+    lib = gdn.lib
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7919 + seed)
+
+    def bf(*shape, std=1.0):
+        return (std * torch.randn(*shape, generator=gen, device=dev)).to(torch.bfloat16)
+
+    def i32(a):
+        return torch.as_tensor(np.asarray(a, np.int32), device=dev)
+
+    def u8(a):
+        return torch.as_tensor(np.asarray(a, np.uint8), device=dev)
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError("%s: %s" % (what, lib.gdn_last_error().decode()))
+
+    def timed(calls):
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(2_000_000)
+        e0.record(stream)
+        for i in range(reps):
+            calls[i % len(calls)]()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    def entry(us, nbytes, nflops=None, **extra):
+        d = {"avg_launch_us": us, "algorithmic_bytes": nbytes, "gb_per_s": nbytes / us / 1e3,
+             "hbm_frac": nbytes / us / 1e3 / HBM_PEAK_GBS}
+        if nflops:
+            d["tflop_per_s"] = nflops / us / 1e6
+        d.update(extra)
+        return d
+
+    out = {}
+    w, b = bf(C, K, std=0.5), bf(C, std=0.1)
+
+    # A1: varlen conv, 2 sequences x 1024 tokens, 256 descriptors, zero initial state
+    T2 = 2048
+    qsl2 = np.array([0, 1024, 2048], np.int32)
+    ch2 = gdn.gdn_build_conv_chunks(qsl2)
+    ch2_d, qsl2_d = i32(ch2.reshape(-1)), i32(qsl2)
+    idx2, hi2 = i32([17, 42]), u8([0, 0])
+    cs = torch.zeros(SLOTS, 3, C, dtype=torch.bfloat16, device=dev)
+    sets = [(bf(T2, C), torch.empty(T2, C, dtype=torch.bfloat16, device=dev)) for _ in range(10)]
+    calls = [lambda x=x, y=y: check(lib.gdn_causal_conv1d_varlen(
+        x.data_ptr(), C, w.data_ptr(), b.data_ptr(), cs.data_ptr(), SLOTS, qsl2_d.data_ptr(), idx2.data_ptr(),
+        hi2.data_ptr(), ch2_d.data_ptr(), len(ch2), y.data_ptr(), C, 2, T2, C, K, 1, sptr), "conv_varlen")
+        for x, y in sets]
+    out["conv_varlen"] = entry(timed(calls), bytes_conv_varlen(T2, 2, 0, len(ch2)),
+                               shape="2 x 1024 tokens, 8192 channels, 256 descriptors", buffer_sets=len(sets))
+    del sets, calls
+
+    # A2 + A3 at the decode shape: 32 sequences, 16 q/k heads, 32 v heads, d = 128
+    B = 32
+    idx_d = i32(np.random.default_rng(seed).permutation(SLOTS)[:B])
+    pools = []
+    for _ in range(6):
+        st = (torch.randn(SLOTS, HV, D, D, generator=gen, device=dev) / np.sqrt(D)).contiguous()
+        pools.append(dict(state=st, cs=bf(SLOTS, 3, C), x=bf(B, C), q=bf(B, HK, D), k=bf(B, HK, D),
+                          v=bf(B, HV, D), o=torch.empty(B, HV, D, dtype=torch.bfloat16, device=dev),
+                          y=torch.empty(B, C, dtype=torch.bfloat16, device=dev)))
+    g = -torch.nn.functional.softplus(torch.randn(B, HV, generator=gen, device=dev)).contiguous()
+    beta = torch.sigmoid(torch.randn(B, HV, generator=gen, device=dev)).contiguous()
+    f1 = ctypes.c_float(1.0)
+    calls = [lambda p=p: check(lib.gdn_fused_conv_decode(
+        p["x"].data_ptr(), C, w.data_ptr(), b.data_ptr(), p["cs"].data_ptr(), SLOTS, g.data_ptr(), beta.data_ptr(),
+        p["state"].data_ptr(), SLOTS, idx_d.data_ptr(), p["o"].data_ptr(), HV * D, None, 0, B, HK, HV, D, D, 1,
+        f1, 1, sptr), "fused_decode") for p in pools]
+    out["fused_decode"] = entry(timed(calls), bytes_fused_decode(B), flops_recurrent(B),
+                                shape="32 sequences x 1 token: conv update on 8192 channels + gated delta rule, "
+                                      "16 q/k heads, 32 v heads, d 128", buffer_sets=len(pools))
+    calls = [lambda p=p: check(lib.gdn_fused_recurrent_decode(
+        p["q"].data_ptr(), HK * D, p["k"].data_ptr(), HK * D, p["v"].data_ptr(), HV * D, g.data_ptr(),
+        beta.data_ptr(), p["state"].data_ptr(), SLOTS, None, idx_d.data_ptr(), None, p["o"].data_ptr(), HV * D,
+        B, B, HK, HV, D, D, f1, 1, sptr), "recurrent_decode") for p in pools]
+    out["recurrent_decode"] = entry(timed(calls), bytes_recurrent(B, B, B), flops_recurrent(B),
+                                    shape="32 sequences x 1 token, 16 q/k heads, 32 v heads, d 128",
+                                    buffer_sets=len(pools))
+    calls = [lambda p=p: check(lib.gdn_causal_conv1d_update(
+        p["x"].data_ptr(), C, w.data_ptr(), b.data_ptr(), p["cs"].data_ptr(), SLOTS, idx_d.data_ptr(),
+        p["y"].data_ptr(), C, B, C, K, 1, sptr), "conv_update") for p in pools]
+    out["conv_update"] = entry(timed(calls), bytes_conv_update(B), shape="32 rows x 8192 channels",
+                               buffer_sets=len(pools), note="launch-bound")
+    del calls
+
+    # A4: chunkwise recurrence at the mixed-step shape (3 prefill chunks summing to 2019 tokens)
+    lens = synth._mixed_lengths(synth.rng(seed, 3, synth.T_LEN))
+    T3 = int(sum(lens))
+    qsl3 = i32(np.concatenate([[0], np.cumsum(lens)]))
+    idx3, hi3 = i32([5, 33, 60]), u8([0, 0, 1])
+    ws_bytes = gdn.gdn_chunk_workspace_size(3, T3, HK, HV)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    g3 = -torch.nn.functional.softplus(torch.randn(T3, HV, generator=gen, device=dev)).contiguous()
+    b3 = torch.sigmoid(torch.randn(T3, HV, generator=gen, device=dev)).contiguous()
+    sets = []
+    for p in pools[:4]:
+        sets.append((bf(T3, C), p["state"], torch.empty(T3, HV, D, dtype=torch.bfloat16, device=dev)))
+    calls = [lambda y=y, st=st, o=o: check(lib.gdn_chunk_gated_delta_rule(
+        y.data_ptr(), C, y.data_ptr() + HK * D * 2, C, y.data_ptr() + 2 * HK * D * 2, C, g3.data_ptr(),
+        b3.data_ptr(), st.data_ptr(), SLOTS, qsl3.data_ptr(), idx3.data_ptr(), hi3.data_ptr(), o.data_ptr(), HV * D,
+        3, T3, HK, HV, D, D, ws.data_ptr(), ws_bytes, f1, 1, sptr), "recurrent_chunk") for y, st, o in sets]
+    us = timed(calls)
+    out["recurrent_chunk"] = entry(us, bytes_recurrent(T3, 1, 3), flops_recurrent(T3),
+                                   shape="3 prefill chunks of %s tokens, 16 q/k heads, 32 v heads, d 128"
+                                         % "+".join(str(x) for x in lens),
+                                   buffer_sets=len(sets), tokens_per_s=T3 / us * 1e6,
+                                   bound="latency (serial over 64-token chunks)")
+    del sets, calls, pools
+    torch.cuda.synchronize()
+    return out
+
 
 def cpu_baseline(seed, n_req, seq_len):
     import oracle
@@ -358,7 +535,8 @@ def main():
     else:
         achieved = nb / (ms_dom * 1e-3) / 1e9
         roof = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_per_launch(dominant),
+                "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "avg_launch_us": avg_us, "algorithmic_per_launch": nb / n, "timed_runs_per_step": n_ev // 2}
 
     ms_per_step = 1e3 * wall / args.steps
@@ -376,6 +554,8 @@ def main():
         "roofline": roof,
         "kernels": kern,
     }
+    if not args.no_isolated:
+        out["isolated"] = isolated(args.seed)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_sample_requests, trace.seq_len)
     line = json.dumps(out)

@@ -101,12 +101,10 @@ __device__ __forceinline__ void split4(const f32x4 &v, bf16x4 &hi, bf16x4 &lo) {
 
 __device__ __forceinline__ void st4(__bf16 *p, const bf16x4 &v) { *reinterpret_cast<bf16x4 *>(p) = v; }
 
-// Workspace and final-state stores are streaming (nontemporal): each element
-// is written once per launch, so no dirty lines of this launch are left in
-// the caches for the next kernel to write back.
-__device__ __forceinline__ void st4_stream(__bf16 *p, const bf16x4 &v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<bf16x4 *>(p));
-}
+// Full-line workspace stores (T, K^T) and the final state are streaming
+// (nontemporal): written once per launch, they leave no dirty lines behind
+// for the next kernel to write back.  P is written in 32-byte pieces per
+// row and stays on plain stores, which the L2 merges into whole lines.
 __device__ __forceinline__ void st8_stream(__bf16 *p, const bf16x8 &v) {
     __builtin_nontemporal_store(v, reinterpret_cast<bf16x8 *>(p));
 }
@@ -256,8 +254,8 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
             const int i0 = 16 * c + 4 * lq;
             if (c > w) {
                 const bf16x4 z = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-                st4_stream(&rec->Phi[t][i0], z);
-                st4_stream(&rec->Plo[t][i0], z);
+                st4(&rec->Phi[t][i0], z);
+                st4(&rec->Plo[t][i0], z);
                 continue;
             }
             f32x4 kk = {0.f, 0.f, 0.f, 0.f}, kq = {0.f, 0.f, 0.f, 0.f};
@@ -280,8 +278,8 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
             *reinterpret_cast<f32x4 *>(&sm.A[t][i0]) = av;
             bf16x4 ph, pl;
             split4(pv, ph, pl);
-            st4_stream(&rec->Phi[t][i0], ph);
-            st4_stream(&rec->Plo[t][i0], pl);
+            st4(&rec->Phi[t][i0], ph);
+            st4(&rec->Plo[t][i0], pl);
         }
     }
     __syncthreads();

@@ -1,0 +1,61 @@
+"""Host-side logic of bench.py (no GPU): algorithmic byte counts, the
+traffic records tied to kernel sources, and the one-GPU contract."""
+import importlib.util
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_algorithmic_bytes_at_the_c32_shapes(bench):
+    # 2 x 1024 prefill: x read + y write, two slots written, weights, bias, descriptors, qsl, indices, flags
+    assert bench.bytes_conv_varlen(2048, 2, 0, 256) == 67_291_158
+    # 32-sequence decode: fp32 state read + written (2 x 32 x 2 MiB), q/k/v, o, g, beta
+    assert bench.bytes_recurrent(32, 32, 32) == 135_012_352
+    # fused decode adds the conv update's x, conv_state read + write, weights
+    assert bench.bytes_fused_decode(32) == bench.bytes_recurrent(32, 32, 32) - 32 * (2 * 16 * 128 + 32 * 128) * 2 \
+        + 32 * (8192 * 2 + 2 * 3 * 8192 * 2 + 4) + 8192 * 4 * 2 + 8192 * 2
+    assert bench.flops_recurrent(1) == 6 * 32 * 128 * 128
+
+
+def test_traffic_record_follows_the_sources(bench, tmp_path, monkeypatch):
+    digest = bench.sources_digest("fused_decode")
+    rec = tmp_path / "traffic.md"
+    rec.write_text("text\ntraffic-record kernel=fused_decode fetch_bytes=10 write_bytes=5 sources=%s\n"
+                   "traffic-record kernel=conv_varlen fetch_bytes=1 write_bytes=1 sources=0000000000000000\n"
+                   % digest)
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(rec))
+    assert bench.traffic_per_launch("fused_decode") == 15
+    assert bench.traffic_per_launch("conv_varlen") is None          # measured on other sources
+    assert bench.traffic_per_launch("recurrent_chunk") is None      # never measured
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.md"))
+    assert bench.traffic_per_launch("fused_decode") is None
+
+
+def test_sources_digest_changes_with_a_kernel_file(bench, tmp_path, monkeypatch):
+    csrc = tmp_path / "csrc"
+    csrc.mkdir()
+    for name in bench.KERNEL_SOURCES["conv_varlen"]:
+        (csrc / name).write_text("// " + name)
+    monkeypatch.setattr(bench, "_CSRC", str(csrc))
+    d0 = bench.sources_digest("conv_varlen")
+    (csrc / "conv.hip").write_text("// conv.hip changed")
+    assert bench.sources_digest("conv_varlen") != d0
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
