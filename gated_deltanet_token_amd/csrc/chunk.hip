@@ -42,7 +42,6 @@ constexpr int DVB = 32;         // v rows per scan workgroup
 constexpr int NTH = 256;        // 4 waves
 constexpr int LDK = DKC + 8;    // padded LDS row (bf16) of a [*][128] tile
 constexpr int LDT = CT + 8;     // padded LDS row (bf16) of a [*][64] tile
-constexpr int LDF = CT + 4;     // padded LDS row (fp32) of a [64][64] tile
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -88,15 +87,18 @@ __device__ __forceinline__ void split(float v, __bf16 &hi, __bf16 &lo) {
     lo = (__bf16)(v - (float)hi);
 }
 
-// four fp32 -> hi and lo bf16x4 (8-byte stores)
+// four fp32 -> hi and lo bf16x4 (8-byte stores).  The same values as split()
+// (hi = RNE(v), lo = RNE(v - hi)), converted two at a time with the packed
+// conversion.
 __device__ __forceinline__ void split4(const f32x4 &v, bf16x4 &hi, bf16x4 &lo) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        __bf16 h, l;
-        split(v[e], h, l);
-        hi[e] = h;
-        lo[e] = l;
-    }
+    typedef float f32x2v __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    const bf16x2v h01 = __builtin_convertvector((f32x2v){v[0], v[1]}, bf16x2v);
+    const bf16x2v h23 = __builtin_convertvector((f32x2v){v[2], v[3]}, bf16x2v);
+    const bf16x2v l01 = __builtin_convertvector((f32x2v){v[0] - (float)h01[0], v[1] - (float)h01[1]}, bf16x2v);
+    const bf16x2v l23 = __builtin_convertvector((f32x2v){v[2] - (float)h23[0], v[3] - (float)h23[1]}, bf16x2v);
+    hi = __builtin_shufflevector(h01, h23, 0, 1, 2, 3);
+    lo = __builtin_shufflevector(l01, l23, 0, 1, 2, 3);
 }
 
 __device__ __forceinline__ void st4(__bf16 *p, const bf16x4 &v) { *reinterpret_cast<bf16x4 *>(p) = v; }
@@ -109,31 +111,92 @@ __device__ __forceinline__ void st8_stream(__bf16 *p, const bf16x8 &v) {
     __builtin_nontemporal_store(v, reinterpret_cast<bf16x8 *>(p));
 }
 
-// C += X Y for 16x16 fp32 tiles in LDS; four 16x16x4 fp32 MFMAs
-__device__ __forceinline__ f32x4 mm16_f32(const float (*X)[LDF], int xr, int xc, const float (*Y)[LDF], int yr,
-                                          int yc, f32x4 c, int lane) {
+// A 64 x 64 lower-triangular fp32 matrix in LDS as its ten 16 x 16 blocks
+// (b, c), b >= c, block index b (b + 1) / 2 + c; rows padded to 20 floats
+constexpr int LDB = 20;
+constexpr int NBLK = 10;
+__device__ __forceinline__ constexpr int blk(int b, int c) { return b * (b + 1) / 2 + c; }
+typedef float Blk[16][LDB];
+
+// C += X Y for two 16 x 16 fp32 blocks; four 16x16x4 fp32 MFMAs
+__device__ __forceinline__ f32x4 mm16(const Blk &X, const Blk &Y, f32x4 c, int lane) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        const float a = X[xr + (lane & 15)][xc + (lane >> 4) + 4 * s];
-        const float b = Y[yr + (lane >> 4) + 4 * s][yc + (lane & 15)];
+        const float a = X[lane & 15][(lane >> 4) + 4 * s];
+        const float b = Y[(lane >> 4) + 4 * s][lane & 15];
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     }
     return c;
 }
 
-__device__ __forceinline__ void put16(float (*Z)[LDF], int zr, int zc, const f32x4 &c, float sgn, int lane) {
+__device__ __forceinline__ void put16(Blk &Z, const f32x4 &c, float sgn, int lane) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Z[zr + 4 * (lane >> 4) + i][zc + (lane & 15)] = sgn * c[i];
+    for (int i = 0; i < 4; ++i) Z[4 * (lane >> 4) + i][lane & 15] = sgn * c[i];
+}
+
+// ---------------------------------------------------------------------------
+// where a global chunk index lands in the packed sequences
+// ---------------------------------------------------------------------------
+// Every lane of a wave reads one sequence's bounds at once (64 sequences per
+// round trip) instead of walking the sequences one load after another.
+
+// the sequence s holding packed chunk `gch` and the chunk's index j in it
+// (s = -1 past the last chunk); called by every lane of the wave
+__device__ __forceinline__ void locate_chunk(const int32_t *qsl, int num_seqs, int gch, int &s_out, int &j_out) {
+    const int lane = threadIdx.x & 63;
+    int before = 0;
+    s_out = -1;
+    j_out = 0;
+    for (int s0 = 0; s0 < num_seqs; s0 += 64) {
+        const int q = s0 + lane;
+        const int lo = qsl[min(q, num_seqs)], hi = qsl[min(q + 1, num_seqs)];
+        int incl = q < num_seqs ? chunk_count(hi - lo) : 0;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int up = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += up;
+        }
+        const int total = __shfl(incl, 63, 64);
+        if (gch < before + total) {
+            // lanes whose sequences end at or before the chunk come first
+            const int ls = __popcll(__ballot(before + incl <= gch));
+            const int excl = ls > 0 ? __shfl(incl, ls - 1, 64) : 0;
+            s_out = s0 + ls;
+            j_out = gch - before - excl;
+            return;
+        }
+        before += total;
+    }
+}
+
+// number of chunks of the sequences before s; called by every lane of the wave
+__device__ __forceinline__ int chunks_before(const int32_t *qsl, int s) {
+    const int lane = threadIdx.x & 63;
+    int total = 0;
+    for (int s0 = 0; s0 < s; s0 += 64) {
+        const int q = s0 + lane;
+        const int lo = qsl[min(q, s)], hi = qsl[min(q + 1, s)];
+        int nc = q < s ? chunk_count(hi - lo) : 0;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) nc += __shfl_xor(nc, off, 64);
+        total += nc;
+    }
+    return total;
 }
 
 // ---------------------------------------------------------------------------
 // prep: one workgroup per (chunk, v-head)
 // ---------------------------------------------------------------------------
+// 31 KB, so that five workgroups share a CU and a 2,048-token step's
+// (chunk, v-head) grid runs in one round: the q rows are not staged (the
+// MFMA reads its q fragments from L2), and T reuses the space of the k rows,
+// which are dead once A and P are formed.
 struct PrepSmem {
-    __bf16 K[CT][LDK];
-    __bf16 Q[CT][LDK];
-    float A[CT][LDF];
-    float Tf[CT][LDF];
+    union {
+        __bf16 K[CT][LDK];   // stages 0-1: the chunk's k rows
+        Blk T[NBLK];         // stage 2: T = (I + A)^-1
+    } u;
+    Blk A[NBLK];
     float lam[CT], rk[CT], rq[CT], beta[CT];
 };
 
@@ -144,20 +207,8 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
     const int work = xcd_contiguous(blockIdx.x, gridDim.x);
     const int h = work % HV;
     const int gch = work / HV;                  // global chunk index
-    // locate (sequence, chunk within it)
-    int s = -1, j = 0;
-    {
-        int c = 0;
-        for (int q = 0; q < a.num_seqs; ++q) {
-            const int nc = chunk_count(a.qsl[q + 1] - a.qsl[q]);
-            if (gch < c + nc) {
-                s = q;
-                j = gch - c;
-                break;
-            }
-            c += nc;
-        }
-    }
+    int s, j;                                   // (sequence, chunk within it)
+    locate_chunk(a.qsl, a.num_seqs, gch, s, j);
     if (s < 0 || a.state_indices[s] < 0) return;
     const int t0 = a.qsl[s] + CT * j;
     const int n = min(CT, a.qsl[s + 1] - t0);
@@ -189,8 +240,7 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
         float skk = 0.f, sqq = 0.f;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            *reinterpret_cast<uint4 *>(&sm.K[tok][32 * part + 8 * m]) = kv[m];
-            *reinterpret_cast<uint4 *>(&sm.Q[tok][32 * part + 8 * m]) = qv[m];
+            *reinterpret_cast<uint4 *>(&sm.u.K[tok][32 * part + 8 * m]) = kv[m];
             float kf[8], qf[8];
             unpack8(kv[m], kf);
             unpack8(qv[m], qf);
@@ -237,7 +287,7 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
         const int d = tid >> 1, half = tid & 1;
         bf16x8 col[4];
 #pragma unroll
-        for (int j = 0; j < 32; ++j) col[j >> 3][j & 7] = sm.K[32 * half + j][d];
+        for (int j = 0; j < 32; ++j) col[j >> 3][j & 7] = sm.u.K[32 * half + j][d];
         __bf16 *dst = &kts[(int64_t)gch * a.num_k_heads + hk].Kt[d][32 * half];
 #pragma unroll
         for (int m = 0; m < 4; ++m) st8_stream(dst + 8 * m, col[m]);
@@ -245,10 +295,21 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
 
     // ---- stage 1: tiles (i-tile c, t-tile w) of K K^T and K Q^T, laid out
     // so each lane holds 4 consecutive i of one row t of A and of P:
-    // A (fp32) into LDS, P (hi/lo) to the workspace with 8-byte stores
+    // A (fp32) into its LDS block, P (hi/lo) to the workspace with 8-byte stores
     {
         const int t = 16 * w + lr;
         const float lam_t = sm.lam[t], beta_t = sm.beta[t], rk_t = sm.rk[t], rq_t = sm.rq[t];
+        // q rows of t-tile w as B operands, straight from L2 (zero past the chunk end)
+        bf16x8 bq[DKC / 32];
+        {
+            const __bf16 *qrow = reinterpret_cast<const __bf16 *>(a.q) + (int64_t)(t0 + min(t, n - 1)) * a.q_stride +
+                                 hk * DKC + 8 * lq;
+#pragma unroll
+            for (int ks = 0; ks < DKC / 32; ++ks) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(qrow + 32 * ks);
+                bq[ks] = __builtin_bit_cast(bf16x8, t < n ? v : make_uint4(0, 0, 0, 0));
+            }
+        }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int i0 = 16 * c + 4 * lq;
@@ -261,11 +322,10 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
             f32x4 kk = {0.f, 0.f, 0.f, 0.f}, kq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < DKC / 32; ++ks) {
-                const bf16x8 ai = frag(&sm.K[0][0], LDK, 16 * c, 32 * ks, lane);
-                const bf16x8 bk = frag(&sm.K[0][0], LDK, 16 * w, 32 * ks, lane);
-                const bf16x8 bq = frag(&sm.Q[0][0], LDK, 16 * w, 32 * ks, lane);
+                const bf16x8 ai = frag(&sm.u.K[0][0], LDK, 16 * c, 32 * ks, lane);
+                const bf16x8 bk = frag(&sm.u.K[0][0], LDK, 16 * w, 32 * ks, lane);
                 kk = mma(ai, bk, kk);
-                kq = mma(ai, bq, kq);
+                kq = mma(ai, bq[ks], kq);
             }
             f32x4 av, pv;
 #pragma unroll
@@ -275,7 +335,7 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
                 av[e] = i < t ? beta_t * rk_t * sm.rk[i] * decay * kk[e] : 0.f;
                 pv[e] = i <= t ? a.scale * rq_t * sm.rk[i] * decay * kq[e] : 0.f;
             }
-            *reinterpret_cast<f32x4 *>(&sm.A[t][i0]) = av;
+            *reinterpret_cast<f32x4 *>(&sm.A[blk(w, c)][lr][4 * lq]) = av;
             bf16x4 ph, pl;
             split4(pv, ph, pl);
             st4(&rec->Phi[t][i0], ph);
@@ -284,29 +344,22 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
     }
     __syncthreads();
 
-    // ---- stage 2: T = (I + A)^-1
+    // ---- stage 2: T = (I + A)^-1, block by block (T overwrites the k rows)
     {
-        float(*Tf)[LDF] = sm.Tf;
-        float(*Am)[LDF] = sm.A;
         if (lane < 16) {
             // diagonal block w by forward substitution; lane j owns column j
+            const Blk &Ad = sm.A[blk(w, w)];
             float xcol[16];
-            const int b0 = 16 * w;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                float acc = t == lane ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) {
+                float acc = r == lane ? 1.f : 0.f;
 #pragma unroll
-                for (int i = 0; i < t; ++i) acc = __builtin_fmaf(-Am[b0 + t][b0 + i], xcol[i], acc);
-                xcol[t] = acc;
+                for (int i = 0; i < r; ++i) acc = __builtin_fmaf(-Ad[r][i], xcol[i], acc);
+                xcol[r] = acc;
             }
+            Blk &Td = sm.u.T[blk(w, w)];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) Tf[b0 + t][b0 + lane] = xcol[t];
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            if (c <= w) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Tf[16 * w + 4 * lq + i][16 * c + lr] = 0.f;
+            for (int r = 0; r < 16; ++r) Td[r][lane] = xcol[r];
         }
         __syncthreads();
         // T_bc = -T_bb (sum_{c<=m<b} A_bm T_mc); wave c walks down column
@@ -314,23 +367,25 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
         const int c = w;
         for (int b = c + 1; b < 4 && w < 3; ++b) {
             f32x4 m = {0.f, 0.f, 0.f, 0.f};
-            for (int mm = c; mm < b; ++mm) m = mm16_f32(Am, 16 * b, 16 * mm, Tf, 16 * mm, 16 * c, m, lane);
-            put16(Tf, 16 * b, 16 * c, m, 1.f, lane);
+            for (int mm = c; mm < b; ++mm) m = mm16(sm.A[blk(b, mm)], sm.u.T[blk(mm, c)], m, lane);
+            put16(sm.u.T[blk(b, c)], m, 1.f, lane);
             f32x4 t = {0.f, 0.f, 0.f, 0.f};
-            t = mm16_f32(Tf, 16 * b, 16 * b, Tf, 16 * b, 16 * c, t, lane);
-            put16(Tf, 16 * b, 16 * c, t, -1.f, lane);
+            t = mm16(sm.u.T[blk(b, b)], sm.u.T[blk(b, c)], t, lane);
+            put16(sm.u.T[blk(b, c)], t, -1.f, lane);
         }
         __syncthreads();
-        // hi/lo to the workspace, 8 consecutive entries per lane
+        // hi/lo to the workspace, 8 consecutive entries per lane (zero above
+        // the diagonal blocks)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int idx = tid + NTH * e;          // 512 groups of 8
             const int t = idx >> 3, i0 = (idx & 7) * 8;
+            const int bt = t >> 4, bc = i0 >> 4;
             bf16x8 hv, lv;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 __bf16 hi, lo;
-                split(Tf[t][i0 + q], hi, lo);
+                split(bc <= bt ? sm.u.T[blk(bt, min(bc, bt))][t & 15][(i0 & 15) + q] : 0.f, hi, lo);
                 hv[q] = hi;
                 lv[q] = lo;
             }
@@ -366,6 +421,9 @@ __device__ __forceinline__ uint4 mask4(bool keep, const uint4 &v) {
     return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
 }
 
+// dword 3 of a raw (unstructured) buffer resource on gfx950
+constexpr int kBufferFlags = 0x00020000;
+
 __device__ __forceinline__ bf16x8 maskf(bool keep, const bf16x8 &v) {
     return __builtin_bit_cast(bf16x8, mask4(keep, __builtin_bit_cast(uint4, v)));
 }
@@ -385,12 +443,14 @@ __global__ __launch_bounds__(NTH, 2) void chunk_scan_kernel(RecurrentArgs a, con
     const int t_end = a.qsl[s + 1];
     if (t_end <= t_begin) return;
     const int hk = h / (HV / a.num_k_heads);
-    int gch = 0;                                   // global index of this sequence's first chunk
-    for (int q = 0; q < s; ++q) gch += chunk_count(a.qsl[q + 1] - a.qsl[q]);
+    int gch = chunks_before(a.qsl, s);             // global index of this sequence's first chunk
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // the wave index is uniform over the wave: as a scalar, the loops that
+    // stop at it are scalar branches rather than exec-masked regions
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lq = lane >> 4;
     const int kh_off = hk * DKC;
+    const int o_col_bytes = 2 * (h * a.dv + vb * DVB);
     const __bf16 *kbase = reinterpret_cast<const __bf16 *>(a.k) + kh_off;
     const __bf16 *qbase = reinterpret_cast<const __bf16 *>(a.q) + kh_off;
 
@@ -469,6 +529,16 @@ __global__ __launch_bounds__(NTH, 2) void chunk_scan_kernel(RecurrentArgs a, con
         const int g_next = more ? gch_c + 1 : gch_c;
         const ChunkRec *rec_next = recs + (int64_t)g_next * HV + h;
         const KtRec *kt_next = kts + (int64_t)g_next * a.num_k_heads + hk;
+
+        // The chunk's o rows through a buffer resource that covers exactly
+        // them: a padded token (t >= n) stores at the end of the range, where
+        // the hardware range check drops it.  The stores then need no branch,
+        // and no branch means no conservative wait for every load in flight
+        // (this chunk's prefetch included) where the paths merge.
+        const int o_row_bytes = 2 * (int)a.o_stride;
+        const int o_range = n * o_row_bytes;
+        const __amdgpu_buffer_rsrc_t o_rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(a.o + (int64_t)t0 * a.o_stride, (short)0, o_range, kBufferFlags);
 
         // ---- the state entering the chunk -> LDS (hi/lo)
 #pragma unroll
@@ -556,9 +626,8 @@ __global__ __launch_bounds__(NTH, 2) void chunk_scan_kernel(RecurrentArgs a, con
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * w + 4 * lq + i;
-                if (t < n)
-                    a.o[(int64_t)(t0 + t) * a.o_stride + (int64_t)h * a.dv + vb * DVB + 16 * rt + lr] =
-                        f32_to_bf16(acc[i]);
+                const int off = t < n ? (t * o_row_bytes + o_col_bytes + 2 * (16 * rt + lr)) : o_range;
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[i]), o_rsrc, off, 0, 0);
             }
         }
         const float g_c = cur.gc;
