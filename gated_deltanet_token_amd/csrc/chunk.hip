@@ -38,7 +38,6 @@ namespace {
 
 constexpr int CT = 64;          // tokens per chunk
 constexpr int DKC = 128;        // head_k_dim
-constexpr int DVB = 32;         // v rows per scan workgroup
 constexpr int NTH = 256;        // 4 waves
 constexpr int LDK = DKC + 8;    // padded LDS row (bf16) of a [*][128] tile
 constexpr int LDT = CT + 8;     // padded LDS row (bf16) of a [*][64] tile
@@ -405,6 +404,7 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
 // would let three workgroups share a CU; registers are capped at 256 per
 // lane (two waves per SIMD), so two do, which keeps a 3-sequence prefill
 // (384 workgroups) resident at once.
+template <int DVB>
 struct ScanSmem {
     __bf16 Shi[DVB][LDK], Slo[DVB][LDK];     // S0 [r][d]
     __bf16 Rhi[DVB][LDT], Rlo[DVB][LDT];     // R^T [r][t]
@@ -428,9 +428,16 @@ __device__ __forceinline__ bf16x8 maskf(bool keep, const bf16x8 &v) {
     return __builtin_bit_cast(bf16x8, mask4(keep, __builtin_bit_cast(uint4, v)));
 }
 
-__global__ __launch_bounds__(NTH, 2) void chunk_scan_kernel(RecurrentArgs a, const ChunkRec *recs, const KtRec *kts,
-                                                        int n_vblocks) {
-    __shared__ ScanSmem sm;
+// DVB v rows per workgroup (NRT = DVB / 16 row tiles per wave): 32 rows,
+// two workgroups per CU; or 64 rows, one workgroup per CU, when 32-row
+// workgroups would outnumber the CUs (a CU running two of them is what sets
+// the pace; one 64-row workgroup shares each token tile's operand loads
+// between twice the rows).
+template <int DVB>
+__global__ __launch_bounds__(NTH, DVB == 64 ? 1 : 2) void chunk_scan_kernel(RecurrentArgs a, const ChunkRec *recs,
+                                                                            const KtRec *kts, int n_vblocks) {
+    constexpr int NRT = DVB / 16;
+    __shared__ ScanSmem<DVB> sm;
     const int HV = a.num_v_heads;
     const int work = xcd_contiguous(blockIdx.x, gridDim.x);
     const int vb = work % n_vblocks;
@@ -458,10 +465,10 @@ __global__ __launch_bounds__(NTH, 2) void chunk_scan_kernel(RecurrentArgs a, con
     // (d-tile dt, v-row tile rt): tile q = 2*rt + (dt - 2w); lane holds
     // S[16 rt + lr][16 dt + 4 lq .. +3] -- four consecutive dims of one row
     float *S_g = a.state + ((int64_t)slot * HV + h) * (int64_t)a.dv * DKC + (int64_t)vb * DVB * DKC;
-    f32x4 S[4];
+    f32x4 S[2 * NRT];
     const bool init = a.has_init == nullptr || a.has_init[s] != 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2 * NRT; ++q) {
         const int rt = q >> 1, dt = 2 * w + (q & 1);
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         S[q] = init ? load_stream4(&S_g[(16 * rt + lr) * DKC + 16 * dt + 4 * lq]) : z;
@@ -474,7 +481,7 @@ __global__ __launch_bounds__(NTH, 2) void chunk_scan_kernel(RecurrentArgs a, con
         bf16x8 kf[4], qf[4];            // K, Q rows 16w + lr, dims 32 ks + 8 lq ..
         f32x4 sb, sbgr, ssqg, su2;      // factors of tokens 16w + 4lq + i
         float gc;                       // G_C (stored for every token; a per-lane load)
-        uint16_t vraw[2][4];            // v of tokens 16w + 4lq + i, rows 16 rt + lr
+        uint16_t vraw[NRT][4];            // v of tokens 16w + 4lq + i, rows 16 rt + lr
         bf16x8 th[2], tl[2];            // T rows 16w + lr, cols 32 ks + 8 lq ..
         bf16x8 ph[2], pl[2];            // P rows 16w + lr
         bf16x8 ktf[2][2];               // K^T rows 16 (2w + j) + lr
@@ -491,7 +498,7 @@ __global__ __launch_bounds__(NTH, 2) void chunk_scan_kernel(RecurrentArgs a, con
         op.sbgr = *reinterpret_cast<const f32x4 *>(&rec->bgr[t4]);
         op.ssqg = *reinterpret_cast<const f32x4 *>(&rec->sqg[t4]);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 op.vraw[rt][i] = a.v[(int64_t)(c_t0 + min(t4 + i, c_n - 1)) * a.v_stride + (int64_t)h * a.dv +
@@ -542,7 +549,7 @@ __global__ __launch_bounds__(NTH, 2) void chunk_scan_kernel(RecurrentArgs a, con
 
         // ---- the state entering the chunk -> LDS (hi/lo)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 2 * NRT; ++q) {
             const int rt = q >> 1, dt = 2 * w + (q & 1);
             bf16x4 hi, lo;
             split4(S[q], hi, lo);
@@ -554,9 +561,9 @@ __global__ __launch_bounds__(NTH, 2) void chunk_scan_kernel(RecurrentArgs a, con
 
         // ---- R = b v - bgr (K S0^T) -> LDS;  o part = sqg (Q S0^T)
         const bool live = 16 * w + lr < n;
-        f32x4 O[2];
+        f32x4 O[NRT];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
+        for (int rt = 0; rt < NRT; ++rt) {
             f32x4 yk = {0.f, 0.f, 0.f, 0.f}, yq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < DKC / 32; ++ks) {
@@ -585,7 +592,7 @@ __global__ __launch_bounds__(NTH, 2) void chunk_scan_kernel(RecurrentArgs a, con
 
         // ---- U = T R (token tile w; T lower triangular) -> LDS, with U' = u2f U
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
+        for (int rt = 0; rt < NRT; ++rt) {
             f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
@@ -612,7 +619,7 @@ __global__ __launch_bounds__(NTH, 2) void chunk_scan_kernel(RecurrentArgs a, con
 
         // ---- o = part + P U -> output;  S^T = G_C S^T + K^T U'
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
+        for (int rt = 0; rt < NRT; ++rt) {
             f32x4 acc = O[rt];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
@@ -632,7 +639,7 @@ __global__ __launch_bounds__(NTH, 2) void chunk_scan_kernel(RecurrentArgs a, con
         }
         const float g_c = cur.gc;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 2 * NRT; ++q) {
             const int rt = q >> 1, j = q & 1;
             f32x4 acc = S[q] * g_c;
 #pragma unroll
@@ -663,7 +670,7 @@ __global__ __launch_bounds__(NTH, 2) void chunk_scan_kernel(RecurrentArgs a, con
     }
 
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2 * NRT; ++q) {
         const int rt = q >> 1, dt = 2 * w + (q & 1);
         store_stream4(&S_g[(16 * rt + lr) * DKC + 16 * dt + 4 * lq], S[q]);
     }
@@ -686,14 +693,20 @@ hipError_t launch_chunk_recurrent(const RecurrentArgs &a, void *workspace, int n
     KtRec *kts = reinterpret_cast<KtRec *>(reinterpret_cast<char *>(workspace) +
                                            mc * a.num_v_heads * (int64_t)sizeof(ChunkRec));
     const long long prep_blocks = mc * a.num_v_heads;
-    const int nvb = a.dv / DVB;
-    const long long scan_blocks = (long long)a.num_seqs * a.num_v_heads * nvb;
+    constexpr int kCUs = 256;
+    const long long heads = (long long)a.num_seqs * a.num_v_heads;
+    const bool wide = heads * (a.dv / 32) > kCUs && (a.dv % 64) == 0;
+    const int nvb = a.dv / (wide ? 64 : 32);
+    const long long scan_blocks = heads * nvb;
     if (scan_blocks == 0) return hipSuccess;
     if (prep_blocks > 0x7fffffffLL || scan_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)prep_blocks), dim3(NTH), 0, stream, a, recs, kts, (int)mc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_scan_kernel, dim3((unsigned)scan_blocks), dim3(NTH), 0, stream, a, recs, kts, nvb);
+    if (wide)
+        hipLaunchKernelGGL(chunk_scan_kernel<64>, dim3((unsigned)scan_blocks), dim3(NTH), 0, stream, a, recs, kts, nvb);
+    else
+        hipLaunchKernelGGL(chunk_scan_kernel<32>, dim3((unsigned)scan_blocks), dim3(NTH), 0, stream, a, recs, kts, nvb);
     return hipGetLastError();
 }
 

@@ -116,3 +116,23 @@ def test_chunk_split_vs_whole_within_rounding():
     check_state(st, st_ref, d["state"], d["state_indices"])
     diff = np.abs(o.float().cpu().numpy() - o_w.float().cpu().numpy()).max()
     assert diff <= 2e-2, diff
+
+
+@pytest.mark.parametrize("lens,HK,HV,dv_,hi,pad", [
+    # 9 x 32 heads x 2 blocks of 32 rows would outnumber the CUs: one 64-row
+    # workgroup per (sequence, head)
+    ([0, 1, 63, 64, 65, 100, 17, 128, 30], 16, 32, 64, [1, 0, 1, 1, 0, 1, 0, 1, 1],
+     [False] * 7 + [True, False]),
+    # 3 sequences with 256-row heads: four 64-row workgroups per head
+    ([70, 65, 129], 16, 32, 256, [0, 1, 1], None),
+])
+def test_chunk_wide_workgroups(lens, HK, HV, dv_, hi, pad):
+    S = len(lens)
+    d = synth.random_gdn(35, 80 + S, lens, HK, HV, 128, dv_, num_slots=S + 2, has_init=hi)
+    idx = d["state_indices"].copy()
+    if pad is not None:
+        idx[np.array(pad)] = -1
+    o, st, o_ref, st_ref = run_chunk(d, idx=idx)
+    check_bf16(o, o_ref, "chunk wide o")
+    used = [int(idx[s]) for s in range(S) if lens[s] > 0 and idx[s] >= 0]
+    check_state(st, st_ref, d["state"], used)
