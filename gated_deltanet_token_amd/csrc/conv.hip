@@ -67,9 +67,14 @@ __global__ __launch_bounds__(THREADS) void conv_varlen_kernel(
     const int64_t hstride = first ? (int64_t)channels : x_stride;
 #pragma unroll
     for (int i = 0; i < 3; ++i) h[i] = *reinterpret_cast<const uint4 *>(hp + i * hstride);
+    // Rows 0-4 are read by this program only: streaming loads.  Rows 5-7
+    // are also the next chunk's halo and stay on plain loads, so that the
+    // neighbour finds them in L2.
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i)
-        r[i] = *reinterpret_cast<const uint4 *>(x + (int64_t)(t0 + min(i, n - 1)) * x_stride + c0);
+    for (int i = 0; i < kChunk; ++i) {
+        const uint16_t *p = x + (int64_t)(t0 + min(i, n - 1)) * x_stride + c0;
+        r[i] = i < kChunk - 3 ? load_stream16(p) : *reinterpret_cast<const uint4 *>(p);
+    }
     // (the flag is read unconditionally, from a valid byte, for the same reason as the bias)
     const uint8_t flag = *(has_init != nullptr ? has_init + d.seq : reinterpret_cast<const uint8_t *>(chunks + ci));
     const uint32_t keep = (first && has_init != nullptr && flag == 0) ? 0u : ~0u;

@@ -42,8 +42,13 @@ __device__ __forceinline__ void store_stream4(float *p, f32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
 }
 
-// streaming 16-byte store of 8 bf16 (an output row slice written once)
+// streaming 16-byte access to 8 bf16 (a row slice read or written once)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream16(const uint16_t *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ void store_stream16(uint16_t *p, const uint4 &v) {
     const u32x4 w = {v.x, v.y, v.z, v.w};
