@@ -421,9 +421,6 @@ __device__ __forceinline__ uint4 mask4(bool keep, const uint4 &v) {
     return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
 }
 
-// dword 3 of a raw (unstructured) buffer resource on gfx950
-constexpr int kBufferFlags = 0x00020000;
-
 __device__ __forceinline__ bf16x8 maskf(bool keep, const bf16x8 &v) {
     return __builtin_bit_cast(bf16x8, mask4(keep, __builtin_bit_cast(uint4, v)));
 }

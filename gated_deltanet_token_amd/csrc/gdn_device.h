@@ -106,6 +106,13 @@ __device__ __forceinline__ float group_sum(float x) {
 // ---------------------------------------------------------------------------
 constexpr int kNumXcd = 8;
 
+// dword 3 of a raw (unstructured) buffer resource on gfx950.  A buffer access
+// whose offset lies at or past the resource's byte range is dropped (store)
+// or returns zero (load): masked accesses without a branch.
+constexpr int kBufferFlags = 0x00020000;
+// cache-policy operand of the buffer builtins for a streaming (nt) access
+constexpr int kBufferStream = 2;
+
 __device__ __forceinline__ int xcd_contiguous(int bid, int n) {
     const int xcd = bid % kNumXcd;
     const int local = bid / kNumXcd;

@@ -262,6 +262,48 @@ def test_recurrent_decode_matches_oracle_small_dims():
         check_state(st, st_ref, d["state"], d["state_indices"])
 
 
+DECODE_EDGES = [
+    # S, HK, HV, dk, dv, has_init, padding
+    (5, 1, 4, 128, 128, [1, 0, 1, 1, 0], [False, False, True, False, False]),   # 512 rows: two passes
+    (3, 1, 3, 128, 40, None, None),                                            # 120 rows: ragged pass
+    (4, 2, 4, 16, 24, [0, 1, 1, 0], None),                                     # 4 lanes per row
+    (2, 4, 8, 64, 72, [1, 1], [True, False]),
+    (6, 2, 2, 32, 8, None, None),                                              # one v head per q/k head
+]
+
+
+@pytest.mark.parametrize("S,HK,HV,dk,dv_,hi,pad", DECODE_EDGES)
+def test_decode_edges_and_varlen_launch_bit_exact(S, HK, HV, dk, dv_, hi, pad):
+    """One token per sequence without query_start_loc (the decode launch)
+    against the oracle, and bit for bit against the same tokens given with
+    query_start_loc (the token-loop launch): the per-row arithmetic is the
+    same, only the work split differs."""
+    d = synth.random_gdn(27, 80 + S, [1] * S, HK, HV, dk, dv_, num_slots=S + 3, has_init=hi)
+    idx = d["state_indices"].copy()
+    if pad is not None:
+        idx[np.array(pad)] = -1
+    wq, wv = HK * dk, HV * dv_
+    row = np.zeros((S, 2 * wq + wv + 24), np.uint16)
+    row[:, 0:wq] = d["q"].reshape(S, wq)
+    row[:, wq:2 * wq] = d["k"].reshape(S, wq)
+    row[:, 2 * wq + 16:2 * wq + 16 + wv] = d["v"].reshape(S, wv)
+    rt = dev(row)
+    qt = rt[:, 0:wq].view(S, HK, dk)
+    kt = rt[:, wq:2 * wq].view(S, HK, dk)
+    vt = rt[:, 2 * wq + 16:2 * wq + 16 + wv].view(S, HV, dv_)
+    hi_arr = d["has_init"] if hi else None
+    o, st = gpu_rec(qt, kt, vt, d["g"], d["beta"], d["state"], idx, hi=hi_arr)
+    o_ref, st_ref = oracle.gated_delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], idx,
+                                            None, hi_arr, 1.0, True)
+    check_bf16(o, o_ref, "decode edge o")
+    used = [int(i) for i in idx if i >= 0]
+    check_state(st, st_ref, d["state"], used)
+    o2, st2 = gpu_rec(qt, kt, vt, d["g"], d["beta"], d["state"], idx, qsl=np.arange(S + 1, dtype=np.int32),
+                      hi=hi_arr)
+    assert np.array_equal(bits(o), bits(o2))
+    assert torch.equal(st, st2)
+
+
 # ---------------------------------------------------------------------------
 # split-vs-whole on the GPU: bit-exact (identical per-token arithmetic)
 # ---------------------------------------------------------------------------
