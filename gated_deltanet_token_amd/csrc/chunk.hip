@@ -16,12 +16,12 @@
 //    parts that do not depend on the state -- norms, cumulative decay,
 //    T = (I + A)^-1, P_ti = scale exp(L_t - L_i)(qh_t . kh_i) (i <= t), K^T
 //    -- written to the caller's workspace;
-//  * scan (one workgroup per (sequence, v-head, 32 v rows), serial over the
-//    sequence's chunks): [K;Q] S0^T, R, U = T R, o = S0 part + P U and
-//    S_C^T = G_C S0^T + K^T U', with the state slice held transposed in VGPRs
-//    in the MFMA accumulator layout (so every lane holds 4 consecutive dims
-//    of a row and all LDS / global traffic is 8- or 16-byte vectors) and the
-//    next chunk's inputs prefetched.
+//  * scan (one workgroup per (sequence, v-head, 32 or 64 v rows), serial
+//    over the sequence's chunks, each wave owning 16 v rows): [K;Q] S0^T,
+//    R, U = T R, o = S0 part + P U and S_C^T = G_C S0^T + K^T U', with the
+//    wave's state rows and every intermediate held in VGPRs in the MFMA
+//    accumulator layout, the chunk's shared operands staged in LDS and the
+//    next chunk's prefetched.
 //
 // Precision: products of raw bf16 inputs (K K^T, Q K^T) are exact in the
 // bf16 MFMA with fp32 accumulation.  Every product with an fp32 operand (the
@@ -394,47 +394,80 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
     }
 }
 
-// ---------------------------------------------------------------------------
-// scan: one workgroup per (sequence, v-head, 32 v rows)
-// ---------------------------------------------------------------------------
-// Only data that crosses waves lives in LDS (the state entering the chunk
-// and R, U, U'); every MFMA operand a wave owns (its K / Q / T / P rows, its
-// K^T rows) is loaded straight from global memory / L2 into registers a
-// chunk ahead of use, into the second of two register sets.  45 KB of LDS
-// would let three workgroups share a CU; registers are capped at 256 per
-// lane (two waves per SIMD), so two do, which keeps a 3-sequence prefill
-// (384 workgroups) resident at once.
-template <int DVB>
-struct ScanSmem {
-    __bf16 Shi[DVB][LDK], Slo[DVB][LDK];     // S0 [r][d]
-    __bf16 Rhi[DVB][LDT], Rlo[DVB][LDT];     // R^T [r][t]
-    __bf16 Uhi[DVB][LDT], Ulo[DVB][LDT];     // U^T [r][t]
-    __bf16 U2hi[DVB][LDT], U2lo[DVB][LDT];   // U'^T [r][t]
-};
-
-// operand fragment straight from global memory (row-major, `ld` elements)
-__device__ __forceinline__ bf16x8 gfrag(const __bf16 *base, int64_t ld, int row, int k0, int lane) {
-    return *reinterpret_cast<const bf16x8 *>(base + (int64_t)row * ld + k0 + 8 * (lane >> 4));
-}
-
 __device__ __forceinline__ uint4 mask4(bool keep, const uint4 &v) {
     return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
 }
 
-__device__ __forceinline__ bf16x8 maskf(bool keep, const bf16x8 &v) {
-    return __builtin_bit_cast(bf16x8, mask4(keep, __builtin_bit_cast(uint4, v)));
+// ---------------------------------------------------------------------------
+// scan, row-split form: one workgroup per (sequence, v-head, 16 NW v rows),
+// wave w owning 16 v rows with the whole chain of a chunk in its registers
+// ---------------------------------------------------------------------------
+// Every product of a chunk is a product of an operand shared by the whole
+// workgroup (K, Q, K^T, T, P: the chunk's, staged once in LDS) with a
+// wave-private one (the wave's state rows, then R, U, U' of its rows):
+//   Y_k = K S_w^T, Y_q = Q S_w^T         (64 tokens x 16 rows, over 128 dims)
+//   R = b v - bgr Y_k,  U = T R,  o = sqg Y_q + P U,
+//   S_w^T <- G_C S_w^T + K^T (u2f U)     (128 dims x 16 rows, over 64 tokens)
+// The wave-private operand is always the B side, taken straight from the
+// previous product's accumulators: an accumulator tile gives lane l the
+// elements (4 (l / 16) + i, l % 16), i < 4, so two tiles stacked along the
+// contraction index give lane l the contraction positions 4 (l / 16) + i and
+// 16 + 4 (l / 16) + i of a 32-wide block.  The shared A side is read from LDS
+// with the same positions (two 8-byte pieces per fragment), so no
+// accumulator ever goes through LDS and no barrier separates the phases.
+// The waves meet twice per chunk, to restage the next chunk's operands
+// (prefetched into registers while the current chunk runs).
+template <int NW>
+struct RowScanSmem {
+    alignas(16) __bf16 K[CT][LDK];                   // [t][d]
+    alignas(16) __bf16 Q[CT][LDK];
+    alignas(16) __bf16 Kt[DKC][LDT];                 // [d][t]
+    alignas(16) __bf16 Th[CT][LDT];                  // [t][i]
+    alignas(16) __bf16 Tl[CT][LDT];
+    alignas(16) __bf16 Ph[CT][LDT];
+    alignas(16) __bf16 Pl[CT][LDT];
+    alignas(16) __bf16 V[CT][16 * NW + 8];           // [t][r], this workgroup's rows
+    alignas(16) float sc[5][CT];                     // beta, bgr, sqg, u2f, G_C
+};
+
+// A-side fragment whose contraction positions follow two stacked
+// accumulator tiles: element e of lane l is (row r0 + l % 16, column
+// k0 + 4 (l / 16) + e) for e < 4 and column k0 + 16 + 4 (l / 16) + e - 4 for e >= 4
+__device__ __forceinline__ bf16x8 afrag(const __bf16 *base, int ld, int r0, int k0, int lane) {
+    const __bf16 *p = base + (r0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
+    const bf16x4 y = *reinterpret_cast<const bf16x4 *>(p + 16);
+    return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// DVB v rows per workgroup (NRT = DVB / 16 row tiles per wave): 32 rows,
-// two workgroups per CU; or 64 rows, one workgroup per CU, when 32-row
-// workgroups would outnumber the CUs (a CU running two of them is what sets
-// the pace; one 64-row workgroup shares each token tile's operand loads
-// between twice the rows).
-template <int DVB>
-__global__ __launch_bounds__(NTH, DVB == 64 ? 1 : 2) void chunk_scan_kernel(RecurrentArgs a, const ChunkRec *recs,
-                                                                            const KtRec *kts, int n_vblocks) {
-    constexpr int NRT = DVB / 16;
-    __shared__ ScanSmem<DVB> sm;
+// B-side fragment (hi and lo bf16 parts) from two accumulator tiles stacked
+// along the contraction index
+__device__ __forceinline__ void bsplit(const f32x4 &x0, const f32x4 &x1, bf16x8 &hi, bf16x8 &lo) {
+    bf16x4 h0, l0, h1, l1;
+    split4(x0, h0, l0);
+    split4(x1, h1, l1);
+    hi = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+    lo = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int NW>
+struct RowStage {
+    static constexpr int NT = 64 * NW, DVB = 16 * NW;
+    static constexpr int NK = CT * DKC / 8 / NT;          // K (and Q, K^T) vectors per thread
+    static constexpr int NTP = CT * CT / 8 / NT;          // T hi (and lo, P hi, P lo) vectors per thread
+    static constexpr int NV = CT * DVB / 8 / NT;          // v vectors per thread
+    uint4 k[NK], q[NK], kt[NK];
+    uint4 th[NTP], tl[NTP], ph[NTP], pl[NTP];
+    uint4 v[NV];
+    uint4 sc;                                          // threads < 80: 4 scalars of one of 5 arrays
+};
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void chunk_scan_rows_kernel(RecurrentArgs a, const ChunkRec *recs,
+                                                                     const KtRec *kts, int n_vblocks) {
+    using St = RowStage<NW>;
+    constexpr int NT = St::NT, DVB = St::DVB;
+    __shared__ RowScanSmem<NW> sm;
     const int HV = a.num_v_heads;
     const int work = xcd_contiguous(blockIdx.x, gridDim.x);
     const int vb = work % n_vblocks;
@@ -447,230 +480,238 @@ __global__ __launch_bounds__(NTH, DVB == 64 ? 1 : 2) void chunk_scan_kernel(Recu
     const int t_end = a.qsl[s + 1];
     if (t_end <= t_begin) return;
     const int hk = h / (HV / a.num_k_heads);
-    int gch = chunks_before(a.qsl, s);             // global index of this sequence's first chunk
+    const int gch0 = chunks_before(a.qsl, s);
 
-    // the wave index is uniform over the wave: as a scalar, the loops that
-    // stop at it are scalar branches rather than exec-masked regions
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lr = lane & 15, lq = lane >> 4;
-    const int kh_off = hk * DKC;
-    const int o_col_bytes = 2 * (h * a.dv + vb * DVB);
-    const __bf16 *kbase = reinterpret_cast<const __bf16 *>(a.k) + kh_off;
-    const __bf16 *qbase = reinterpret_cast<const __bf16 *>(a.q) + kh_off;
+    const int lr = lane & 15, g = lane >> 4;
+    const int r0 = vb * DVB;                         // the workgroup's first v row
+    const int rw = 16 * w + lr;                      // this lane's v row within the workgroup
 
-    // the state slice, transposed, in the accumulator layout of S^T tiles
-    // (d-tile dt, v-row tile rt): tile q = 2*rt + (dt - 2w); lane holds
-    // S[16 rt + lr][16 dt + 4 lq .. +3] -- four consecutive dims of one row
-    float *S_g = a.state + ((int64_t)slot * HV + h) * (int64_t)a.dv * DKC + (int64_t)vb * DVB * DKC;
-    f32x4 S[2 * NRT];
+    // the wave's state rows as the accumulator tiles of S_w^T: tile dt,
+    // lane holds S[r0 + rw][16 dt + 4 g + i]
+    float *S_g = a.state + (((int64_t)slot * HV + h) * a.dv + r0 + rw) * DKC + 4 * g;
+    f32x4 S[8];
     const bool init = a.has_init == nullptr || a.has_init[s] != 0;
 #pragma unroll
-    for (int q = 0; q < 2 * NRT; ++q) {
-        const int rt = q >> 1, dt = 2 * w + (q & 1);
+    for (int dt = 0; dt < 8; ++dt) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        S[q] = init ? load_stream4(&S_g[(16 * rt + lr) * DKC + 16 * dt + 4 * lq]) : z;
+        S[dt] = init ? load_stream4(S_g + 16 * dt) : z;
     }
 
-    // per-lane operands of one chunk.  Two register sets alternate (the
-    // chunk loop is unrolled by two), so the next chunk's loads land in the
-    // other set and nothing has to wait for them before the next chunk.
-    struct Ops {
-        bf16x8 kf[4], qf[4];            // K, Q rows 16w + lr, dims 32 ks + 8 lq ..
-        f32x4 sb, sbgr, ssqg, su2;      // factors of tokens 16w + 4lq + i
-        float gc;                       // G_C (stored for every token; a per-lane load)
-        uint16_t vraw[NRT][4];            // v of tokens 16w + 4lq + i, rows 16 rt + lr
-        bf16x8 th[2], tl[2];            // T rows 16w + lr, cols 32 ks + 8 lq ..
-        bf16x8 ph[2], pl[2];            // P rows 16w + lr
-        bf16x8 ktf[2][2];               // K^T rows 16 (2w + j) + lr
+    // the operands of a chunk, global -> registers (rows past the chunk end
+    // read its last token and are zeroed, so padded tokens are exact no-ops),
+    // in four parts issued at the start of the four phases of the chunk
+    // before: all at once they filled the memory pipeline and held the wave
+    // at the issue for ~2,000 cycles
+    auto fetch_kq = [&](St &st, int t0, int n) {
+#pragma unroll
+        for (int j = 0; j < St::NK; ++j) {
+            const int idx = tid + NT * j, t = idx >> 4, c = (idx & 15) * 8;
+            const int64_t row = t0 + min(t, n - 1);
+            const uint4 kv = *reinterpret_cast<const uint4 *>(a.k + row * a.k_stride + hk * DKC + c);
+            const uint4 qv = *reinterpret_cast<const uint4 *>(a.q + row * a.q_stride + hk * DKC + c);
+            st.k[j] = mask4(t < n, kv);
+            st.q[j] = mask4(t < n, qv);
+        }
     };
-    auto load_y = [&](Ops &op, int c_t0, int c_n, const ChunkRec *rec) {
-        const int row = c_t0 + min(16 * w + lr, c_n - 1);
+    auto fetch_kt = [&](St &st, int gch) {
+        const KtRec *kt = kts + (int64_t)gch * a.num_k_heads + hk;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            op.kf[ks] = gfrag(kbase, a.k_stride, row, 32 * ks, lane);
-            op.qf[ks] = gfrag(qbase, a.q_stride, row, 32 * ks, lane);
+        for (int j = 0; j < St::NK; ++j) {
+            const int idx = tid + NT * j, d = idx >> 3, ct = (idx & 7) * 8;
+            st.kt[j] = *reinterpret_cast<const uint4 *>(&kt->Kt[d][ct]);
         }
-        const int t4 = 16 * w + 4 * lq;
-        op.sb = *reinterpret_cast<const f32x4 *>(&rec->beta[t4]);
-        op.sbgr = *reinterpret_cast<const f32x4 *>(&rec->bgr[t4]);
-        op.ssqg = *reinterpret_cast<const f32x4 *>(&rec->sqg[t4]);
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                op.vraw[rt][i] = a.v[(int64_t)(c_t0 + min(t4 + i, c_n - 1)) * a.v_stride + (int64_t)h * a.dv +
-                                     vb * DVB + 16 * rt + lr];
     };
-    auto load_t = [&](Ops &op, const ChunkRec *rec) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            op.th[ks] = gfrag(&rec->Thi[0][0], CT, 16 * w + lr, 32 * ks, lane);
-            op.tl[ks] = gfrag(&rec->Tlo[0][0], CT, 16 * w + lr, 32 * ks, lane);
-        }
-        op.su2 = *reinterpret_cast<const f32x4 *>(&rec->u2f[16 * w + 4 * lq]);
-    };
-    auto load_p = [&](Ops &op, const ChunkRec *rec, const KtRec *kt) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            op.ph[ks] = gfrag(&rec->Phi[0][0], CT, 16 * w + lr, 32 * ks, lane);
-            op.pl[ks] = gfrag(&rec->Plo[0][0], CT, 16 * w + lr, 32 * ks, lane);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                op.ktf[j][ks] = gfrag(&kt->Kt[0][0], CT, 16 * (2 * w + j) + lr, 32 * ks, lane);
-        }
-        op.gc = rec->gC[16 * w + 4 * lq];
-    };
-
-    // one chunk: consumes `cur`, prefetches the next chunk into `nxt`
-    auto chunk = [&](const Ops &cur, Ops &nxt, int t0, int gch_c) {
-        const int n = min(CT, t_end - t0);
-        // the next chunk's operands; the last chunk reloads its own (always
-        // in bounds, and the loads stay unconditional: no branch for the
-        // wait-count tracking to merge)
-        const bool more = t0 + CT < t_end;
-        const int t_next = more ? t0 + CT : t0;
-        const int n_next = min(CT, t_end - t_next);
-        const int g_next = more ? gch_c + 1 : gch_c;
-        const ChunkRec *rec_next = recs + (int64_t)g_next * HV + h;
-        const KtRec *kt_next = kts + (int64_t)g_next * a.num_k_heads + hk;
-
-        // The chunk's o rows through a buffer resource that covers exactly
-        // them: a padded token (t >= n) stores at the end of the range, where
-        // the hardware range check drops it.  The stores then need no branch,
-        // and no branch means no conservative wait for every load in flight
-        // (this chunk's prefetch included) where the paths merge.
-        const int o_row_bytes = 2 * (int)a.o_stride;
-        const int o_range = n * o_row_bytes;
-        const __amdgpu_buffer_rsrc_t o_rsrc =
-            __builtin_amdgcn_make_buffer_rsrc(a.o + (int64_t)t0 * a.o_stride, (short)0, o_range, kBufferFlags);
-
-        // ---- the state entering the chunk -> LDS (hi/lo)
-#pragma unroll
-        for (int q = 0; q < 2 * NRT; ++q) {
-            const int rt = q >> 1, dt = 2 * w + (q & 1);
-            bf16x4 hi, lo;
-            split4(S[q], hi, lo);
-            st4(&sm.Shi[16 * rt + lr][16 * dt + 4 * lq], hi);
-            st4(&sm.Slo[16 * rt + lr][16 * dt + 4 * lq], lo);
-        }
-        __syncthreads();
-        load_y(nxt, t_next, n_next, rec_next);     // next chunk's K, Q, v, factors
-
-        // ---- R = b v - bgr (K S0^T) -> LDS;  o part = sqg (Q S0^T)
-        const bool live = 16 * w + lr < n;
-        f32x4 O[NRT];
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-            f32x4 yk = {0.f, 0.f, 0.f, 0.f}, yq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < DKC / 32; ++ks) {
-                const bf16x8 bh = frag(&sm.Shi[0][0], LDK, 16 * rt, 32 * ks, lane);
-                const bf16x8 bl = frag(&sm.Slo[0][0], LDK, 16 * rt, 32 * ks, lane);
-                const bf16x8 ka = maskf(live, cur.kf[ks]), qa = maskf(live, cur.qf[ks]);
-                yk = mma(ka, bh, yk);
-                yq = mma(qa, bh, yq);
-                yk = mma(ka, bl, yk);
-                yq = mma(qa, bl, yq);
-            }
-            f32x4 r;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float vv = 16 * w + 4 * lq + i < n ? bf16_to_f32(cur.vraw[rt][i]) : 0.f;
-                r[i] = cur.sb[i] * vv - cur.sbgr[i] * yk[i];
-                O[rt][i] = cur.ssqg[i] * yq[i];
-            }
-            bf16x4 hi, lo;
-            split4(r, hi, lo);
-            st4(&sm.Rhi[16 * rt + lr][16 * w + 4 * lq], hi);
-            st4(&sm.Rlo[16 * rt + lr][16 * w + 4 * lq], lo);
-        }
-        __syncthreads();
-        load_t(nxt, rec_next);
-
-        // ---- U = T R (token tile w; T lower triangular) -> LDS, with U' = u2f U
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-            f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (ks > (w >> 1)) break;
-                const bf16x8 bh = frag(&sm.Rhi[0][0], LDT, 16 * rt, 32 * ks, lane);
-                const bf16x8 bl = frag(&sm.Rlo[0][0], LDT, 16 * rt, 32 * ks, lane);
-                u = mma(cur.th[ks], bh, u);
-                u = mma(cur.th[ks], bl, u);
-                u = mma(cur.tl[ks], bh, u);
-            }
-            f32x4 u2;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) u2[i] = cur.su2[i] * u[i];
-            bf16x4 hi, lo;
-            split4(u, hi, lo);
-            st4(&sm.Uhi[16 * rt + lr][16 * w + 4 * lq], hi);
-            st4(&sm.Ulo[16 * rt + lr][16 * w + 4 * lq], lo);
-            split4(u2, hi, lo);
-            st4(&sm.U2hi[16 * rt + lr][16 * w + 4 * lq], hi);
-            st4(&sm.U2lo[16 * rt + lr][16 * w + 4 * lq], lo);
-        }
-        __syncthreads();
-        load_p(nxt, rec_next, kt_next);
-
-        // ---- o = part + P U -> output;  S^T = G_C S^T + K^T U'
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-            f32x4 acc = O[rt];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (ks > (w >> 1)) break;
-                const bf16x8 bh = frag(&sm.Uhi[0][0], LDT, 16 * rt, 32 * ks, lane);
-                const bf16x8 bl = frag(&sm.Ulo[0][0], LDT, 16 * rt, 32 * ks, lane);
-                acc = mma(cur.ph[ks], bh, acc);
-                acc = mma(cur.ph[ks], bl, acc);
-                acc = mma(cur.pl[ks], bh, acc);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * w + 4 * lq + i;
-                const int off = t < n ? (t * o_row_bytes + o_col_bytes + 2 * (16 * rt + lr)) : o_range;
-                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[i]), o_rsrc, off, 0, 0);
-            }
-        }
-        const float g_c = cur.gc;
-#pragma unroll
-        for (int q = 0; q < 2 * NRT; ++q) {
-            const int rt = q >> 1, j = q & 1;
-            f32x4 acc = S[q] * g_c;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 bh = frag(&sm.U2hi[0][0], LDT, 16 * rt, 32 * ks, lane);
-                const bf16x8 bl = frag(&sm.U2lo[0][0], LDT, 16 * rt, 32 * ks, lane);
-                acc = mma(cur.ktf[j][ks], bh, acc);
-                acc = mma(cur.ktf[j][ks], bl, acc);
-            }
-            S[q] = acc;
-        }
-        // no barrier: the next chunk writes S (read only before the second
-        // barrier above), then R, U, U' only after barriers every wave passes
-        // once it is done with this chunk
-    };
-
-    Ops A, B;
-    {
+    auto fetch_t = [&](St &st, int gch) {
         const ChunkRec *rec = recs + (int64_t)gch * HV + h;
-        load_y(A, t_begin, min(CT, t_end - t_begin), rec);
-        load_t(A, rec);
-        load_p(A, rec, kts + (int64_t)gch * a.num_k_heads + hk);
+#pragma unroll
+        for (int j = 0; j < St::NTP; ++j) {
+            const int idx = tid + NT * j, t = idx >> 3, c = (idx & 7) * 8;
+            st.th[j] = *reinterpret_cast<const uint4 *>(&rec->Thi[t][c]);
+            st.tl[j] = *reinterpret_cast<const uint4 *>(&rec->Tlo[t][c]);
+        }
+    };
+    auto fetch_pv = [&](St &st, int t0, int n, int gch) {
+        const ChunkRec *rec = recs + (int64_t)gch * HV + h;
+#pragma unroll
+        for (int j = 0; j < St::NTP; ++j) {
+            const int idx = tid + NT * j, t = idx >> 3, c = (idx & 7) * 8;
+            st.ph[j] = *reinterpret_cast<const uint4 *>(&rec->Phi[t][c]);
+            st.pl[j] = *reinterpret_cast<const uint4 *>(&rec->Plo[t][c]);
+        }
+#pragma unroll
+        for (int j = 0; j < St::NV; ++j) {
+            const int idx = tid + NT * j, t = idx / (DVB / 8), c = (idx % (DVB / 8)) * 8;
+            const uint4 vv = *reinterpret_cast<const uint4 *>(a.v + (int64_t)(t0 + min(t, n - 1)) * a.v_stride +
+                                                              (int64_t)h * a.dv + r0 + c);
+            st.v[j] = mask4(t < n, vv);
+        }
+        // beta, bgr, sqg, u2f, G_C: 5 x 64 consecutive floats of the record
+        st.sc = *reinterpret_cast<const uint4 *>(&rec->beta[0] + 4 * min(tid, 79));
+    };
+    auto stage = [&](const St &st) {
+#pragma unroll
+        for (int j = 0; j < St::NK; ++j) {
+            const int idx = tid + NT * j, t = idx >> 4, c = (idx & 15) * 8;
+            *reinterpret_cast<uint4 *>(&sm.K[t][c]) = st.k[j];
+            *reinterpret_cast<uint4 *>(&sm.Q[t][c]) = st.q[j];
+            const int d = idx >> 3, ct = (idx & 7) * 8;
+            *reinterpret_cast<uint4 *>(&sm.Kt[d][ct]) = st.kt[j];
+        }
+#pragma unroll
+        for (int j = 0; j < St::NTP; ++j) {
+            const int idx = tid + NT * j, t = idx >> 3, c = (idx & 7) * 8;
+            *reinterpret_cast<uint4 *>(&sm.Th[t][c]) = st.th[j];
+            *reinterpret_cast<uint4 *>(&sm.Tl[t][c]) = st.tl[j];
+            *reinterpret_cast<uint4 *>(&sm.Ph[t][c]) = st.ph[j];
+            *reinterpret_cast<uint4 *>(&sm.Pl[t][c]) = st.pl[j];
+        }
+#pragma unroll
+        for (int j = 0; j < St::NV; ++j) {
+            const int idx = tid + NT * j, t = idx / (DVB / 8), c = (idx % (DVB / 8)) * 8;
+            *reinterpret_cast<uint4 *>(&sm.V[t][c]) = st.v[j];
+        }
+        if (tid < 80) *reinterpret_cast<uint4 *>(&sm.sc[0][0] + 4 * tid) = st.sc;
+    };
+
+    const int o_col_bytes = 2 * (h * a.dv + r0 + rw);
+    const int o_row_bytes = 2 * (int)a.o_stride;
+
+    St st;
+    {
+        const int n0 = min(CT, t_end - t_begin);
+        fetch_kq(st, t_begin, n0);
+        fetch_kt(st, gch0);
+        fetch_t(st, gch0);
+        fetch_pv(st, t_begin, n0, gch0);
     }
-    for (int t0 = t_begin; t0 < t_end; t0 += 2 * CT, gch += 2) {
-        chunk(A, B, t0, gch);
-        if (t0 + CT >= t_end) break;
-        chunk(B, A, t0 + CT, gch + 1);
+    stage(st);
+    __syncthreads();
+
+    int gch = gch0;
+    for (int t0 = t_begin; t0 < t_end; t0 += CT, ++gch) {
+        const int n = min(CT, t_end - t0);
+        // the next chunk's operands; the last chunk fetches its own again
+        // (in bounds, and unconditional: a load behind a branch would make
+        // the compiler wait for it where the paths merge, before this chunk)
+        const bool more = t0 + CT < t_end;
+        const int t_next = more ? t0 + CT : t0, n_next = min(CT, t_end - t_next);
+        const int g_next = more ? gch + 1 : gch;
+        fetch_kq(st, t_next, n_next);
+
+        // ---- Y_k = K S_w^T, Y_q = Q S_w^T (token tiles tt)
+        f32x4 yk[4], yq[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) yk[tt] = yq[tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            bf16x8 bh, bl;
+            bsplit(S[2 * kb], S[2 * kb + 1], bh, bl);
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const bf16x8 ka = afrag(&sm.K[0][0], LDK, 16 * tt, 32 * kb, lane);
+                const bf16x8 qa = afrag(&sm.Q[0][0], LDK, 16 * tt, 32 * kb, lane);
+                yk[tt] = mma(ka, bh, yk[tt]);
+                yq[tt] = mma(qa, bh, yq[tt]);
+                yk[tt] = mma(ka, bl, yk[tt]);
+                yq[tt] = mma(qa, bl, yq[tt]);
+            }
+        }
+        // ---- R = b v - bgr Y_k; the o part sqg Y_q
+        f32x4 R[4], O[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int t4 = 16 * tt + 4 * g;
+            const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&sm.sc[0][t4]);
+            const f32x4 bgr4 = *reinterpret_cast<const f32x4 *>(&sm.sc[1][t4]);
+            const f32x4 sqg4 = *reinterpret_cast<const f32x4 *>(&sm.sc[2][t4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float vv = bf16_to_f32(__builtin_bit_cast(uint16_t, sm.V[t4 + i][rw]));
+                R[tt][i] = b4[i] * vv - bgr4[i] * yk[tt][i];
+                O[tt][i] = sqg4[i] * yq[tt][i];
+            }
+        }
+        // ---- U = T R (T lower triangular: token tile tt needs blocks ib <= tt / 2); U' = u2f U
+        f32x4 U[4], U2[4];
+        fetch_kt(st, g_next);
+        {
+            bf16x8 rh[2], rl[2];
+            bsplit(R[0], R[1], rh[0], rl[0]);
+            bsplit(R[2], R[3], rh[1], rl[1]);
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ib = 0; ib <= tt / 2; ++ib) {
+                    const bf16x8 th = afrag(&sm.Th[0][0], LDT, 16 * tt, 32 * ib, lane);
+                    const bf16x8 tl = afrag(&sm.Tl[0][0], LDT, 16 * tt, 32 * ib, lane);
+                    u = mma(th, rh[ib], u);
+                    u = mma(th, rl[ib], u);
+                    u = mma(tl, rh[ib], u);
+                }
+                U[tt] = u;
+                const f32x4 u2f4 = *reinterpret_cast<const f32x4 *>(&sm.sc[3][16 * tt + 4 * g]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) U2[tt][i] = u2f4[i] * u[i];
+            }
+        }
+        // ---- o = sqg Y_q + P U -> output (tokens past the chunk end fall
+        // outside the buffer range and are dropped)
+        fetch_t(st, g_next);
+        {
+            const int o_range = n * o_row_bytes;
+            const __amdgpu_buffer_rsrc_t o_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                a.o + (int64_t)t0 * a.o_stride, (short)0, o_range, kBufferFlags);
+            bf16x8 uh[2], ul[2];
+            bsplit(U[0], U[1], uh[0], ul[0]);
+            bsplit(U[2], U[3], uh[1], ul[1]);
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                f32x4 acc = O[tt];
+#pragma unroll
+                for (int ib = 0; ib <= tt / 2; ++ib) {
+                    const bf16x8 ph = afrag(&sm.Ph[0][0], LDT, 16 * tt, 32 * ib, lane);
+                    const bf16x8 pl = afrag(&sm.Pl[0][0], LDT, 16 * tt, 32 * ib, lane);
+                    acc = mma(ph, uh[ib], acc);
+                    acc = mma(ph, ul[ib], acc);
+                    acc = mma(pl, uh[ib], acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * tt + 4 * g + i;
+                    const int off = t < n ? t * o_row_bytes + o_col_bytes : o_range;
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[i]), o_rsrc, off, 0, 0);
+                }
+            }
+        }
+        // ---- S_w^T = G_C S_w^T + K^T U'
+        fetch_pv(st, t_next, n_next, g_next);
+        {
+            const float g_c = sm.sc[4][0];
+            bf16x8 vh[2], vl[2];
+            bsplit(U2[0], U2[1], vh[0], vl[0]);
+            bsplit(U2[2], U2[3], vh[1], vl[1]);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                f32x4 acc = S[dt] * g_c;
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) {
+                    const bf16x8 ka = afrag(&sm.Kt[0][0], LDT, 16 * dt, 32 * tb, lane);
+                    acc = mma(ka, vh[tb], acc);
+                    acc = mma(ka, vl[tb], acc);
+                }
+                S[dt] = acc;
+            }
+        }
+        if (!more) break;
+        __syncthreads();                 // every wave is done with this chunk's operands
+        stage(st);
+        __syncthreads();
     }
 
 #pragma unroll
-    for (int q = 0; q < 2 * NRT; ++q) {
-        const int rt = q >> 1, dt = 2 * w + (q & 1);
-        store_stream4(&S_g[(16 * rt + lr) * DKC + 16 * dt + 4 * lq], S[q]);
-    }
+    for (int dt = 0; dt < 8; ++dt) store_stream4(S_g + 16 * dt, S[dt]);
 }
 
 }  // namespace
@@ -701,9 +742,11 @@ hipError_t launch_chunk_recurrent(const RecurrentArgs &a, void *workspace, int n
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (wide)
-        hipLaunchKernelGGL(chunk_scan_kernel<64>, dim3((unsigned)scan_blocks), dim3(NTH), 0, stream, a, recs, kts, nvb);
+        hipLaunchKernelGGL(chunk_scan_rows_kernel<4>, dim3((unsigned)scan_blocks), dim3(256), 0, stream, a, recs, kts,
+                           nvb);
     else
-        hipLaunchKernelGGL(chunk_scan_kernel<32>, dim3((unsigned)scan_blocks), dim3(NTH), 0, stream, a, recs, kts, nvb);
+        hipLaunchKernelGGL(chunk_scan_rows_kernel<2>, dim3((unsigned)scan_blocks), dim3(128), 0, stream, a, recs, kts,
+                           nvb);
     return hipGetLastError();
 }
 
