@@ -47,10 +47,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // ---------------------------------------------------------------------------
 // workspace records
 // ---------------------------------------------------------------------------
-// per (chunk, v-head): T hi, T lo, P hi, P lo ([64][64] bf16 each, [t][i]),
-// then per-token scalars
+// per (chunk, v-head): T hi, T lo, P hi, P lo -- lower triangular, so only
+// their ten 16 x 16 blocks (b, c), b >= c, block index b (b + 1) / 2 + c,
+// each [16][16] bf16 ([t][i]) -- then per-token scalars
+constexpr int NBLK16 = 10;
 struct ChunkRec {
-    __bf16 Thi[CT][CT], Tlo[CT][CT], Phi[CT][CT], Plo[CT][CT];
+    __bf16 TP[4][NBLK16][16][16];   // T hi, T lo, P hi, P lo
     float beta[CT];   // b_t
     float bgr[CT];    // b_t G_t rk_t          (R = b v - bgr (K S0^T))
     float sqg[CT];    // scale rq_t G_t        (o = sqg (Q S0^T) + P U)
@@ -139,13 +141,16 @@ __device__ __forceinline__ void put16(Blk &Z, const f32x4 &c, float sgn, int lan
 // Every lane of a wave reads one sequence's bounds at once (64 sequences per
 // round trip) instead of walking the sequences one load after another.
 
-// the sequence s holding packed chunk `gch` and the chunk's index j in it
-// (s = -1 past the last chunk); called by every lane of the wave
-__device__ __forceinline__ void locate_chunk(const int32_t *qsl, int num_seqs, int gch, int &s_out, int &j_out) {
+// the sequence s holding packed chunk `gch`, the chunk's index j in it and
+// the sequence's token range [lo, hi) (s = -1 past the last chunk); called
+// by every lane of the wave
+__device__ __forceinline__ void locate_chunk(const int32_t *qsl, int num_seqs, int gch, int &s_out, int &j_out,
+                                             int &lo_out, int &hi_out) {
     const int lane = threadIdx.x & 63;
     int before = 0;
     s_out = -1;
     j_out = 0;
+    lo_out = hi_out = 0;
     for (int s0 = 0; s0 < num_seqs; s0 += 64) {
         const int q = s0 + lane;
         const int lo = qsl[min(q, num_seqs)], hi = qsl[min(q + 1, num_seqs)];
@@ -162,6 +167,8 @@ __device__ __forceinline__ void locate_chunk(const int32_t *qsl, int num_seqs, i
             const int excl = ls > 0 ? __shfl(incl, ls - 1, 64) : 0;
             s_out = s0 + ls;
             j_out = gch - before - excl;
+            lo_out = __shfl(lo, ls, 64);
+            hi_out = __shfl(hi, ls, 64);
             return;
         }
         before += total;
@@ -206,11 +213,13 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
     const int work = xcd_contiguous(blockIdx.x, gridDim.x);
     const int h = work % HV;
     const int gch = work / HV;                  // global chunk index
-    int s, j;                                   // (sequence, chunk within it)
-    locate_chunk(a.qsl, a.num_seqs, gch, s, j);
-    if (s < 0 || a.state_indices[s] < 0) return;
-    const int t0 = a.qsl[s] + CT * j;
-    const int n = min(CT, a.qsl[s + 1] - t0);
+    int s, j, lo, hi;                           // (sequence, chunk within it, its tokens)
+    locate_chunk(a.qsl, a.num_seqs, gch, s, j, lo, hi);
+    // (a padded sequence, state index < 0, is prepared too: its records are
+    // never read, and the row loads need not wait for the index)
+    if (s < 0) return;
+    const int t0 = lo + CT * j;
+    const int n = min(CT, hi - t0);
     const int grp = HV / a.num_k_heads;
     const int hk = h / grp;
 
@@ -312,12 +321,7 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int i0 = 16 * c + 4 * lq;
-            if (c > w) {
-                const bf16x4 z = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-                st4(&rec->Phi[t][i0], z);
-                st4(&rec->Plo[t][i0], z);
-                continue;
-            }
+            if (c > w) continue;                    // above the diagonal blocks: not stored
             f32x4 kk = {0.f, 0.f, 0.f, 0.f}, kq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < DKC / 32; ++ks) {
@@ -337,8 +341,8 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
             *reinterpret_cast<f32x4 *>(&sm.A[blk(w, c)][lr][4 * lq]) = av;
             bf16x4 ph, pl;
             split4(pv, ph, pl);
-            st4(&rec->Phi[t][i0], ph);
-            st4(&rec->Plo[t][i0], pl);
+            st4(&rec->TP[2][blk(w, c)][lr][4 * lq], ph);
+            st4(&rec->TP[3][blk(w, c)][lr][4 * lq], pl);
         }
     }
     __syncthreads();
@@ -373,23 +377,23 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
             put16(sm.u.T[blk(b, c)], t, -1.f, lane);
         }
         __syncthreads();
-        // hi/lo to the workspace, 8 consecutive entries per lane (zero above
-        // the diagonal blocks)
+        // hi/lo to the workspace, the ten blocks only, 8 consecutive entries per lane
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const int idx = tid + NTH * e;          // 512 groups of 8
-            const int t = idx >> 3, i0 = (idx & 7) * 8;
-            const int bt = t >> 4, bc = i0 >> 4;
-            bf16x8 hv, lv;
+            const int idx = tid + NTH * e;          // 320 groups of 8
+            if (idx < NBLK16 * 32) {
+                const int b = idx >> 5, r = (idx >> 1) & 15, c0 = (idx & 1) * 8;
+                bf16x8 hv, lv;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                __bf16 hi, lo;
-                split(bc <= bt ? sm.u.T[blk(bt, min(bc, bt))][t & 15][(i0 & 15) + q] : 0.f, hi, lo);
-                hv[q] = hi;
-                lv[q] = lo;
+                for (int q = 0; q < 8; ++q) {
+                    __bf16 hi, lo;
+                    split(sm.u.T[b][r][c0 + q], hi, lo);
+                    hv[q] = hi;
+                    lv[q] = lo;
+                }
+                st8_stream(&rec->TP[0][b][r][c0], hv);
+                st8_stream(&rec->TP[1][b][r][c0], lv);
             }
-            st8_stream(&rec->Thi[t][i0], hv);
-            st8_stream(&rec->Tlo[t][i0], lv);
         }
     }
 }
@@ -460,10 +464,10 @@ template <int NW>
 struct RowStage {
     static constexpr int NT = 64 * NW, DVB = 16 * NW;
     static constexpr int NK = CT * DKC / 8 / NT;          // K (and Q, K^T) vectors per thread
-    static constexpr int NTP = CT * CT / 8 / NT;          // T hi (and lo, P hi, P lo) vectors per thread
+    static constexpr int NTP = 4 * NBLK16 * 32 / NT;      // 16-byte pieces of the T and P blocks per thread
     static constexpr int NV = CT * DVB / 8 / NT;          // v vectors per thread
     uint4 k[NK], q[NK], kt[NK];
-    uint4 th[NTP], tl[NTP], ph[NTP], pl[NTP];
+    uint4 tp[NTP];
     uint4 v[NV];
     uint4 sc;                                          // threads < 80: 4 scalars of one of 5 arrays
 };
@@ -528,23 +532,15 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_scan_rows_kernel(RecurrentAr
             st.kt[j] = *reinterpret_cast<const uint4 *>(&kt->Kt[d][ct]);
         }
     };
+    // T and P: the record's ten blocks of each of the four matrices are
+    // 1280 consecutive 16-byte pieces
     auto fetch_t = [&](St &st, int gch) {
-        const ChunkRec *rec = recs + (int64_t)gch * HV + h;
+        const uint4 *src = reinterpret_cast<const uint4 *>(&recs[(int64_t)gch * HV + h].TP[0][0][0][0]);
 #pragma unroll
-        for (int j = 0; j < St::NTP; ++j) {
-            const int idx = tid + NT * j, t = idx >> 3, c = (idx & 7) * 8;
-            st.th[j] = *reinterpret_cast<const uint4 *>(&rec->Thi[t][c]);
-            st.tl[j] = *reinterpret_cast<const uint4 *>(&rec->Tlo[t][c]);
-        }
+        for (int j = 0; j < St::NTP; ++j) st.tp[j] = src[tid + NT * j];
     };
     auto fetch_pv = [&](St &st, int t0, int n, int gch) {
         const ChunkRec *rec = recs + (int64_t)gch * HV + h;
-#pragma unroll
-        for (int j = 0; j < St::NTP; ++j) {
-            const int idx = tid + NT * j, t = idx >> 3, c = (idx & 7) * 8;
-            st.ph[j] = *reinterpret_cast<const uint4 *>(&rec->Phi[t][c]);
-            st.pl[j] = *reinterpret_cast<const uint4 *>(&rec->Plo[t][c]);
-        }
 #pragma unroll
         for (int j = 0; j < St::NV; ++j) {
             const int idx = tid + NT * j, t = idx / (DVB / 8), c = (idx % (DVB / 8)) * 8;
@@ -571,11 +567,11 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_scan_rows_kernel(RecurrentAr
         }
 #pragma unroll
         for (int j = 0; j < St::NTP; ++j) {
-            const int idx = tid + NT * j, t = idx >> 3, c = (idx & 7) * 8;
-            st16(&sm.Th[t][c], st.th[j]);
-            st16(&sm.Tl[t][c], st.tl[j]);
-            st16(&sm.Ph[t][c], st.ph[j]);
-            st16(&sm.Pl[t][c], st.pl[j]);
+            // piece p: matrix m, block (bt, bc), row r, half hf
+            const int p = tid + NT * j, m = p / (NBLK16 * 32), q = p - m * (NBLK16 * 32);
+            const int b = q >> 5, r = (q >> 1) & 15, hf = q & 1;
+            const int bt = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3, bc = b - bt * (bt + 1) / 2;
+            st16(&sm.Th[0][0] + m * (CT * RLDT) + (16 * bt + r) * RLDT + 16 * bc + 8 * hf, st.tp[j]);
         }
 #pragma unroll
         for (int j = 0; j < St::NV; ++j) {
@@ -588,6 +584,13 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_scan_rows_kernel(RecurrentAr
     const int o_col_bytes = 2 * (h * a.dv + r0 + rw);
     const int o_row_bytes = 2 * (int)a.o_stride;
 
+    // the blocks above T's and P's diagonal blocks that the products read,
+    // (0, 1) and (2, 3), are zero; the restaging never writes them
+    for (int e = tid; e < 4 * 2 * 16 * 2; e += NT) {
+        const int m = e >> 6, z = (e >> 5) & 1, r = (e >> 1) & 15, hf = e & 1;
+        st16(&sm.Th[0][0] + m * (CT * RLDT) + (16 * (2 * z) + r) * RLDT + 16 * (2 * z + 1) + 8 * hf,
+             make_uint4(0, 0, 0, 0));
+    }
     St st;
     {
         const int n0 = min(CT, t_end - t_begin);

@@ -176,12 +176,13 @@ def test_chunk_validation(kw, code):
 
 
 def test_chunk_workspace_size_formula():
-    # per (64-token chunk, v-head): T and P as hi/lo bf16 (4 x 8 KiB) + 5 x 64
+    # per (64-token chunk, v-head): T and P as hi/lo bf16, the ten 16 x 16
+    # blocks of each lower-triangular 64 x 64 matrix (4 x 10 x 512 B), + 5 x 64
     # fp32 factors; per (chunk, q/k head): K^T (16 KiB); chunks bounded by
     # ceil(T / 64) + S
     for S, T, HK, HV in ((3, 2019, 16, 32), (1, 1, 1, 1), (2, 2048, 16, 32), (0, 0, 16, 32)):
         mc = (T + 63) // 64 + S
-        assert gdn.gdn_chunk_workspace_size(S, T, HK, HV) == mc * (HV * (4 * 8192 + 5 * 256) + HK * 16384)
+        assert gdn.gdn_chunk_workspace_size(S, T, HK, HV) == mc * (HV * (4 * 10 * 512 + 5 * 256) + HK * 16384)
 
 
 def fused(**kw):
