@@ -136,3 +136,20 @@ def test_chunk_wide_workgroups(lens, HK, HV, dv_, hi, pad):
     check_bf16(o, o_ref, "chunk wide o")
     used = [int(idx[s]) for s in range(S) if lens[s] > 0 and idx[s] >= 0]
     check_state(st, st_ref, d["state"], used)
+
+
+def test_chunk_many_sequences():
+    """More than 64 sequences (empty ones and a padded one among them): the
+    chunk -> sequence lookup and the first-chunk offset walk the sequences 64
+    at a time."""
+    lens = [(i * 37) % 45 for i in range(70)]
+    lens[5] = 130
+    S = len(lens)
+    hi = [i % 3 != 0 for i in range(S)]
+    d = synth.random_gdn(36, 77, lens, 2, 4, 128, 64, num_slots=S + 2, has_init=hi)
+    idx = d["state_indices"].copy()
+    idx[66] = -1
+    o, st, o_ref, st_ref = run_chunk(d, idx=idx)
+    check_bf16(o, o_ref, "chunk many-sequence o")
+    used = [int(idx[s]) for s in range(S) if lens[s] > 0 and idx[s] >= 0]
+    check_state(st, st_ref, d["state"], used)
