@@ -119,8 +119,9 @@ def test_chunk_split_vs_whole_within_rounding():
 
 
 @pytest.mark.parametrize("lens,HK,HV,dv_,hi,pad", [
-    # 9 x 32 heads x 2 blocks of 32 rows would outnumber the CUs: one 64-row
-    # workgroup per (sequence, head)
+    # 64-row workgroups (head_v_dim a multiple of 64): one per (sequence, head)
+    # at dv 64, four per head at dv 256; dv 32 and 96 elsewhere take the
+    # 32-row form
     ([0, 1, 63, 64, 65, 100, 17, 128, 30], 16, 32, 64, [1, 0, 1, 1, 0, 1, 0, 1, 1],
      [False] * 7 + [True, False]),
     # 3 sequences with 256-row heads: four 64-row workgroups per head
