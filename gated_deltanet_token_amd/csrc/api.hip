@@ -210,6 +210,9 @@ GDN_EXPORT int gdn_chunk_gated_delta_rule(const gdn_bf16 *q, int64_t q_stride, c
     if (rc) return rc;
     if (head_k_dim != 128) return fail(GDN_ERR_UNSUPPORTED, "chunked form: head_k_dim must be 128");
     if (head_v_dim % 32) return fail(GDN_ERR_UNSUPPORTED, "chunked form: head_v_dim must be a multiple of 32");
+    // the kernels address a 64-token chunk's rows with 32-bit byte offsets
+    if (q_stride >= (1 << 24) || k_stride >= (1 << 24) || v_stride >= (1 << 24) || o_stride >= (1 << 24))
+        return fail(GDN_ERR_UNSUPPORTED, "chunked form: token strides must be below 2^24 elements");
     const size_t need = (size_t)gdn::chunk_workspace_bytes(num_seqs, num_tokens, num_k_heads, num_v_heads);
     if (!workspace) return fail(GDN_ERR_INVALID, "workspace is required (%zu bytes)", need);
     if (((uintptr_t)workspace & 255u) != 0) return fail(GDN_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");

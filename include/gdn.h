@@ -242,13 +242,15 @@ int gdn_fused_recurrent_decode(const gdn_bf16 *q, int64_t q_stride,
  *   query_start_loc  required (int32 [num_seqs + 1])
  *   head_k_dim       must be 128
  *   head_v_dim       a positive multiple of 32 up to 256
+ *   q/k/v/o_stride   below 2^24 elements (32-bit offsets within a chunk)
  *   workspace        device scratch owned by the caller, 256-byte aligned,
  *                    at least gdn_chunk_workspace_size(num_seqs, num_tokens,
  *                    num_k_heads, num_v_heads) bytes; its contents on entry
  *                    do not matter and are overwritten.  Calls that share a
  *                    workspace must not overlap in time.
  * Errors beyond those: GDN_ERR_INVALID (NULL workspace), GDN_ERR_UNSUPPORTED
- * (misaligned workspace), GDN_ERR_CAPACITY (workspace_bytes too small).
+ * (misaligned workspace, a token stride of 2^24 elements or more),
+ * GDN_ERR_CAPACITY (workspace_bytes too small).
  * Results equal the per-token recurrence up to fp32 rounding (a different
  * association of the same sums); sequence lengths need not be multiples of
  * 64.  Splitting a sequence across calls moves the chunk boundaries, so it

@@ -170,6 +170,7 @@ def chunk(**kw):
     (dict(qsl=None), INV), (dict(q=None), INV), (dict(HV=24), INV), (dict(o=V), INV),
     (dict(dk=64), UNS), (dict(dk=16), UNS), (dict(dv=48), UNS), (dict(dv=512), UNS), (dict(q=Q + 8), UNS),
     (dict(ws=None), INV), (dict(ws=WS + 128), UNS), (dict(wsb=WS_NEED - 1), CAP),
+    (dict(os=1 << 24), UNS),     # 32-bit byte offsets within a 64-token chunk
 ])
 def test_chunk_validation(kw, code):
     assert chunk(**kw) == code, gdn.lib.gdn_last_error()
