@@ -421,12 +421,20 @@ __device__ __forceinline__ uint4 mask4(bool keep, const uint4 &v) {
 // accumulator ever goes through LDS and no barrier separates the phases.
 // The waves meet twice per chunk, to restage the next chunk's operands
 // (prefetched into registers while the current chunk runs).
-// Rows padded by 4 bf16 (8 bytes), so that a fragment read -- 8 bytes from
-// each of 16 consecutive rows -- lands in 16 different 8-byte bank pairs
-// (row pitch = 8 mod 128 bytes); 16-byte padding puts rows r and r + 8 on
-// the same banks (measured 4% slower at the mixed step).
-constexpr int RLDK = DKC + 4;
-constexpr int RLDT = CT + 4;
+// Within every 32-column block of a staged A-side tile the columns are
+// stored permuted, so that the eight columns a lane group g takes (4 g .. 4 g
+// + 3 and 16 + 4 g .. 16 + 4 g + 3) sit side by side at 8 g .. 8 g + 7: a
+// fragment is one aligned 16-byte read.  Column c of a block is stored at
+// 8 ((c % 16) / 4) + 4 (c / 16) + c % 4; eight consecutive columns 8 h .. 8 h
+// + 7 (h < 4) therefore land as two 4-column halves at pstart(h) and
+// pstart(h) + 8.  Rows padded by 8 bf16 (16 bytes): eight consecutive rows
+// of a 16-byte fragment read then fall on eight different 16-byte bank
+// groups (row pitch = 16 mod 128 bytes).
+constexpr int RLDK = DKC + 8;
+constexpr int RLDT = CT + 8;
+__device__ __forceinline__ int pstart(int c8) {       // c8: first column of 8, a multiple of 8
+    return (c8 & ~31) + 16 * ((c8 >> 3) & 1) + 4 * ((c8 >> 4) & 1);
+}
 template <int NW>
 struct RowScanSmem {
     alignas(16) __bf16 K[CT][RLDK];                  // [t][d]
@@ -442,12 +450,10 @@ struct RowScanSmem {
 
 // A-side fragment whose contraction positions follow two stacked
 // accumulator tiles: element e of lane l is (row r0 + l % 16, column
-// k0 + 4 (l / 16) + e) for e < 4 and column k0 + 16 + 4 (l / 16) + e - 4 for e >= 4
+// k0 + 4 (l / 16) + e) for e < 4 and column k0 + 16 + 4 (l / 16) + e - 4 for
+// e >= 4 -- in the permuted block layout, the 8 elements from k0 + 8 (l / 16)
 __device__ __forceinline__ bf16x8 afrag(const __bf16 *base, int ld, int r0, int k0, int lane) {
-    const __bf16 *p = base + (r0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
-    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
-    const bf16x4 y = *reinterpret_cast<const bf16x4 *>(p + 16);
-    return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+    return *reinterpret_cast<const bf16x8 *>(base + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
 }
 
 // B-side fragment (hi and lo bf16 parts) from two accumulator tiles stacked
@@ -551,19 +557,21 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_scan_rows_kernel(RecurrentAr
         // beta, bgr, sqg, u2f, G_C: 5 x 64 consecutive floats of the record
         st.sc = *reinterpret_cast<const uint4 *>(&rec->beta[0] + 4 * min(tid, 79));
     };
-    // (the padded rows are 8-byte aligned: each 16-byte piece goes in two halves)
-    auto st16 = [](__bf16 *p, const uint4 &v) {
-        reinterpret_cast<uint2 *>(p)[0] = make_uint2(v.x, v.y);
-        reinterpret_cast<uint2 *>(p)[1] = make_uint2(v.z, v.w);
+    // 8 consecutive columns c8 .. c8 + 7 of a row: two 4-column halves, 8
+    // positions apart in the permuted block layout
+    auto st16 = [](__bf16 *row, int c8, const uint4 &v) {
+        __bf16 *p = row + pstart(c8);
+        *reinterpret_cast<uint2 *>(p) = make_uint2(v.x, v.y);
+        *reinterpret_cast<uint2 *>(p + 8) = make_uint2(v.z, v.w);
     };
     auto stage = [&](const St &st) {
 #pragma unroll
         for (int j = 0; j < St::NK; ++j) {
             const int idx = tid + NT * j, t = idx >> 4, c = (idx & 15) * 8;
-            st16(&sm.K[t][c], st.k[j]);
-            st16(&sm.Q[t][c], st.q[j]);
+            st16(sm.K[t], c, st.k[j]);
+            st16(sm.Q[t], c, st.q[j]);
             const int d = idx >> 3, ct = (idx & 7) * 8;
-            st16(&sm.Kt[d][ct], st.kt[j]);
+            st16(sm.Kt[d], ct, st.kt[j]);
         }
 #pragma unroll
         for (int j = 0; j < St::NTP; ++j) {
@@ -571,7 +579,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_scan_rows_kernel(RecurrentAr
             const int p = tid + NT * j, m = p / (NBLK16 * 32), q = p - m * (NBLK16 * 32);
             const int b = q >> 5, r = (q >> 1) & 15, hf = q & 1;
             const int bt = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3, bc = b - bt * (bt + 1) / 2;
-            st16(&sm.Th[0][0] + m * (CT * RLDT) + (16 * bt + r) * RLDT + 16 * bc + 8 * hf, st.tp[j]);
+            st16(&sm.Th[0][0] + m * (CT * RLDT) + (16 * bt + r) * RLDT, 16 * bc + 8 * hf, st.tp[j]);
         }
 #pragma unroll
         for (int j = 0; j < St::NV; ++j) {
@@ -588,7 +596,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_scan_rows_kernel(RecurrentAr
     // (0, 1) and (2, 3), are zero; the restaging never writes them
     for (int e = tid; e < 4 * 2 * 16 * 2; e += NT) {
         const int m = e >> 6, z = (e >> 5) & 1, r = (e >> 1) & 15, hf = e & 1;
-        st16(&sm.Th[0][0] + m * (CT * RLDT) + (16 * (2 * z) + r) * RLDT + 16 * (2 * z + 1) + 8 * hf,
+        st16(&sm.Th[0][0] + m * (CT * RLDT) + (16 * (2 * z) + r) * RLDT, 16 * (2 * z + 1) + 8 * hf,
              make_uint4(0, 0, 0, 0));
     }
     St st;
