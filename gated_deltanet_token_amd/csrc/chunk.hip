@@ -398,10 +398,6 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
     }
 }
 
-__device__ __forceinline__ uint4 mask4(bool keep, const uint4 &v) {
-    return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
-}
-
 // ---------------------------------------------------------------------------
 // scan, row-split form: one workgroup per (sequence, v-head, 16 NW v rows),
 // wave w owning 16 v rows with the whole chain of a chunk in its registers
@@ -514,20 +510,20 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_scan_rows_kernel(RecurrentAr
         S[dt] = init ? load_stream4(S_g + 16 * dt) : z;
     }
 
-    // the operands of a chunk, global -> registers (rows past the chunk end
-    // read its last token and are zeroed, so padded tokens are exact no-ops),
-    // in four parts issued at the start of the four phases of the chunk
-    // before: all at once they filled the memory pipeline and held the wave
-    // at the issue for ~2,000 cycles
+    // the operands of a chunk, global -> registers, in four parts issued at
+    // the start of the four phases of the chunk before: all at once they
+    // filled the memory pipeline and held the wave at the issue for ~2,000
+    // cycles.  Rows past the chunk end read its last token again (finite
+    // values, not zeroed): the prep gives a padded token beta = bgr = 0, a
+    // zero gate and a zero K^T column, so its R, U and U' are exactly zero
+    // and its Y rows, computed from the repeated token, are never used.
     auto fetch_kq = [&](St &st, int t0, int n) {
 #pragma unroll
         for (int j = 0; j < St::NK; ++j) {
             const int idx = tid + NT * j, t = idx >> 4, c = (idx & 15) * 8;
             const int64_t row = t0 + min(t, n - 1);
-            const uint4 kv = *reinterpret_cast<const uint4 *>(a.k + row * a.k_stride + hk * DKC + c);
-            const uint4 qv = *reinterpret_cast<const uint4 *>(a.q + row * a.q_stride + hk * DKC + c);
-            st.k[j] = mask4(t < n, kv);
-            st.q[j] = mask4(t < n, qv);
+            st.k[j] = *reinterpret_cast<const uint4 *>(a.k + row * a.k_stride + hk * DKC + c);
+            st.q[j] = *reinterpret_cast<const uint4 *>(a.q + row * a.q_stride + hk * DKC + c);
         }
     };
     auto fetch_kt = [&](St &st, int gch) {
@@ -550,9 +546,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_scan_rows_kernel(RecurrentAr
 #pragma unroll
         for (int j = 0; j < St::NV; ++j) {
             const int idx = tid + NT * j, t = idx / (DVB / 8), c = (idx % (DVB / 8)) * 8;
-            const uint4 vv = *reinterpret_cast<const uint4 *>(a.v + (int64_t)(t0 + min(t, n - 1)) * a.v_stride +
-                                                              (int64_t)h * a.dv + r0 + c);
-            st.v[j] = mask4(t < n, vv);
+            st.v[j] = *reinterpret_cast<const uint4 *>(a.v + (int64_t)(t0 + min(t, n - 1)) * a.v_stride +
+                                                       (int64_t)h * a.dv + r0 + c);
         }
         // beta, bgr, sqg, u2f, G_C: 5 x 64 consecutive floats of the record
         st.sc = *reinterpret_cast<const uint4 *>(&rec->beta[0] + 4 * min(tid, 79));
@@ -678,8 +673,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_scan_rows_kernel(RecurrentAr
                 for (int i = 0; i < 4; ++i) U2[tt][i] = u2f4[i] * u[i];
             }
         }
-        // ---- o = sqg Y_q + P U -> output (tokens past the chunk end fall
-        // outside the buffer range and are dropped)
+        // ---- o = sqg Y_q + P U -> output (rows past the chunk end fall
+        // outside the buffer range, so the hardware drops their stores)
         fetch_t(st, g_next);
         {
             const int o_range = n * o_row_bytes;
@@ -700,11 +695,9 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_scan_rows_kernel(RecurrentAr
                     acc = mma(pl, uh[ib], acc);
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * tt + 4 * g + i;
-                    const int off = t < n ? t * o_row_bytes + o_col_bytes : o_range;
-                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[i]), o_rsrc, off, 0, 0);
-                }
+                for (int i = 0; i < 4; ++i)
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[i]), o_rsrc,
+                                                          (16 * tt + 4 * g + i) * o_row_bytes + o_col_bytes, 0, 0);
             }
         }
         // ---- S_w^T = G_C S_w^T + K^T U'
