@@ -191,28 +191,37 @@ __device__ __forceinline__ int chunks_before(const int32_t *qsl, int s) {
 }
 
 // ---------------------------------------------------------------------------
-// prep: one workgroup per (chunk, v-head)
+// prep: one workgroup per (chunk, VPW v-heads of one q/k head)
 // ---------------------------------------------------------------------------
-// 31 KB, so that five workgroups share a CU and a 2,048-token step's
-// (chunk, v-head) grid runs in one round: the q rows are not staged (the
-// MFMA reads its q fragments from L2), and T reuses the space of the k rows,
-// which are dead once A and P are formed.
+// The v-heads that share a q/k head share the chunk's k and q rows, their
+// norms and the products K K^T and Q K^T; only the gates and betas -- so A,
+// T and P -- are per v-head.  With two v-heads per workgroup (VPW = 2, an
+// even number of v-heads per q/k head) eight waves form the shared part once
+// and each v-head gets four waves for its inversion; the ten tiles of K K^T
+// and Q K^T go round-robin over the waves (at most two per wave).  The q
+// rows are not staged (the MFMA reads its q fragments from L2), and T reuses
+// the space of the k rows, which are dead once A and P are formed: 53 KB at
+// VPW = 2 (three workgroups per CU), 31 KB at VPW = 1 (five).
+template <int VPW>
 struct PrepSmem {
     union {
         __bf16 K[CT][LDK];   // stages 0-1: the chunk's k rows
-        Blk T[NBLK];         // stage 2: T = (I + A)^-1
+        Blk T[VPW][NBLK];    // stage 2: T = (I + A)^-1 per v-head
     } u;
-    Blk A[NBLK];
-    float lam[CT], rk[CT], rq[CT], beta[CT];
+    Blk A[VPW][NBLK];
+    float rk[CT], rq[CT];
+    float lam[VPW][CT], beta[VPW][CT];
 };
 
-__global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkRec *recs, KtRec *kts,
-                                                        int max_chunks) {
-    __shared__ PrepSmem sm;
-    const int HV = a.num_v_heads;
+template <int VPW>
+__global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, ChunkRec *recs, KtRec *kts,
+                                                              int max_chunks) {
+    constexpr int NT = NTH * VPW, NW = NT / 64;
+    __shared__ PrepSmem<VPW> sm;
+    const int HV = a.num_v_heads, NP = HV / VPW;
     const int work = xcd_contiguous(blockIdx.x, gridDim.x);
-    const int h = work % HV;
-    const int gch = work / HV;                  // global chunk index
+    const int h0 = (work % NP) * VPW;           // the workgroup's first v-head
+    const int gch = work / NP;                  // global chunk index
     int s, j, lo, hi;                           // (sequence, chunk within it, its tokens)
     locate_chunk(a.qsl, a.num_seqs, gch, s, j, lo, hi);
     // (a padded sequence, state index < 0, is prepared too: its records are
@@ -221,14 +230,14 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
     const int t0 = lo + CT * j;
     const int n = min(CT, hi - t0);
     const int grp = HV / a.num_k_heads;
-    const int hk = h / grp;
+    const int hk = h0 / grp;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lq = lane >> 4;
-    ChunkRec *rec = recs + (int64_t)gch * HV + h;
 
-    // ---- stage 0: k/q rows, norms, cumulative decay, K^T
-    {
+    // ---- stage 0: k/q rows and norms (first four waves); cumulative decay of
+    // v-head v (wave v)
+    if (tid < NTH) {
         const int tok = tid >> 2, part = tid & 3;
         uint4 kv[4], qv[4];
         if (tok < n) {
@@ -264,8 +273,9 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
             sm.rk[tok] = a.l2norm ? rsqrtf(skk + 1e-6f) : 1.f;
             sm.rq[tok] = a.l2norm ? rsqrtf(sqq + 1e-6f) : 1.f;
         }
-        if (w == 0) {
+        if (w < VPW) {
             // padded tokens: g = 0 and beta = 0 make them exact no-ops
+            const int h = h0 + w;
             float gg = lane < n ? a.g[(int64_t)(t0 + lane) * HV + h] : 0.f;
             const float bb = lane < n ? a.beta[(int64_t)(t0 + lane) * HV + h] : 0.f;
 #pragma unroll
@@ -273,41 +283,45 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
                 const float up = __shfl_up(gg, off, 64);
                 if (lane >= off) gg += up;
             }
-            sm.lam[lane] = gg;
-            sm.beta[lane] = bb;
+            sm.lam[w][lane] = gg;
+            sm.beta[w][lane] = bb;
         }
     }
     __syncthreads();
 
-    // per-token scalars for the scan
-    if (w == 0) {
+    // per-token scalars for the scan (wave v for v-head v)
+    if (w < VPW) {
         const int t = lane;
-        const float lam = sm.lam[t], lamC = sm.lam[CT - 1];
+        ChunkRec *rec = recs + (int64_t)gch * HV + h0 + w;
+        const float lam = sm.lam[w][t], lamC = sm.lam[w][CT - 1];
         const float G = expf(lam), rk = sm.rk[t];
-        rec->beta[t] = sm.beta[t];
-        rec->bgr[t] = sm.beta[t] * G * rk;
+        rec->beta[t] = sm.beta[w][t];
+        rec->bgr[t] = sm.beta[w][t] * G * rk;
         rec->sqg[t] = a.scale * sm.rq[t] * G;
         rec->u2f[t] = expf(lamC - lam) * rk;
         rec->gC[t] = expf(lamC);
     }
-    // K^T for the scan (once per q/k head): lane pair per dim d, 32 tokens each
-    if ((h % grp) == 0) {
-        const int d = tid >> 1, half = tid & 1;
-        bf16x8 col[4];
+    // K^T for the scan (once per q/k head): NT / 128 threads per dim d, each
+    // CT / (NT / 128) consecutive tokens
+    if ((h0 % grp) == 0) {
+        constexpr int PARTS = NT / DKC, TPT = CT / PARTS;
+        const int d = tid / PARTS, part = tid % PARTS;
+        bf16x8 col[TPT / 8];
 #pragma unroll
-        for (int j = 0; j < 32; ++j) col[j >> 3][j & 7] = sm.u.K[32 * half + j][d];
-        __bf16 *dst = &kts[(int64_t)gch * a.num_k_heads + hk].Kt[d][32 * half];
+        for (int jj = 0; jj < TPT; ++jj) col[jj >> 3][jj & 7] = sm.u.K[TPT * part + jj][d];
+        __bf16 *dst = &kts[(int64_t)gch * a.num_k_heads + hk].Kt[d][TPT * part];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) st8_stream(dst + 8 * m, col[m]);
+        for (int m = 0; m < TPT / 8; ++m) st8_stream(dst + 8 * m, col[m]);
     }
 
-    // ---- stage 1: tiles (i-tile c, t-tile w) of K K^T and K Q^T, laid out
-    // so each lane holds 4 consecutive i of one row t of A and of P:
-    // A (fp32) into its LDS block, P (hi/lo) to the workspace with 8-byte stores
-    {
-        const int t = 16 * w + lr;
-        const float lam_t = sm.lam[t], beta_t = sm.beta[t], rk_t = sm.rk[t], rq_t = sm.rq[t];
-        // q rows of t-tile w as B operands, straight from L2 (zero past the chunk end)
+    // ---- stage 1: the ten lower-triangular tiles (t-tile bt, i-tile bc) of
+    // K K^T and K Q^T, round-robin over the waves, laid out so each lane holds
+    // 4 consecutive i of one row t; per v-head, A (fp32) into its LDS block and
+    // P (hi/lo) to the workspace with 8-byte stores
+    for (int b = w; b < NBLK16; b += NW) {
+        const int bt = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3, bc = b - bt * (bt + 1) / 2;
+        const int t = 16 * bt + lr, i0 = 16 * bc + 4 * lq;
+        // q rows of t-tile bt as B operands, straight from L2 (zero past the chunk end)
         bf16x8 bq[DKC / 32];
         {
             const __bf16 *qrow = reinterpret_cast<const __bf16 *>(a.q) + (int64_t)(t0 + min(t, n - 1)) * a.q_stride +
@@ -318,40 +332,43 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
                 bq[ks] = __builtin_bit_cast(bf16x8, t < n ? v : make_uint4(0, 0, 0, 0));
             }
         }
+        f32x4 kk = {0.f, 0.f, 0.f, 0.f}, kq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int i0 = 16 * c + 4 * lq;
-            if (c > w) continue;                    // above the diagonal blocks: not stored
-            f32x4 kk = {0.f, 0.f, 0.f, 0.f}, kq = {0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < DKC / 32; ++ks) {
+            const bf16x8 ai = frag(&sm.u.K[0][0], LDK, 16 * bc, 32 * ks, lane);
+            const bf16x8 bk = frag(&sm.u.K[0][0], LDK, 16 * bt, 32 * ks, lane);
+            kk = mma(ai, bk, kk);
+            kq = mma(ai, bq[ks], kq);
+        }
+        const float rk_t = sm.rk[t], rq_t = sm.rq[t];
 #pragma unroll
-            for (int ks = 0; ks < DKC / 32; ++ks) {
-                const bf16x8 ai = frag(&sm.u.K[0][0], LDK, 16 * c, 32 * ks, lane);
-                const bf16x8 bk = frag(&sm.u.K[0][0], LDK, 16 * w, 32 * ks, lane);
-                kk = mma(ai, bk, kk);
-                kq = mma(ai, bq[ks], kq);
-            }
+        for (int v = 0; v < VPW; ++v) {
+            const float lam_t = sm.lam[v][t], beta_t = sm.beta[v][t];
             f32x4 av, pv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = i0 + e;
-                const float decay = i <= t ? expf(lam_t - sm.lam[i]) : 0.f;
+                const float decay = i <= t ? expf(lam_t - sm.lam[v][i]) : 0.f;
                 av[e] = i < t ? beta_t * rk_t * sm.rk[i] * decay * kk[e] : 0.f;
                 pv[e] = i <= t ? a.scale * rq_t * sm.rk[i] * decay * kq[e] : 0.f;
             }
-            *reinterpret_cast<f32x4 *>(&sm.A[blk(w, c)][lr][4 * lq]) = av;
+            *reinterpret_cast<f32x4 *>(&sm.A[v][b][lr][4 * lq]) = av;
             bf16x4 ph, pl;
             split4(pv, ph, pl);
-            st4(&rec->TP[2][blk(w, c)][lr][4 * lq], ph);
-            st4(&rec->TP[3][blk(w, c)][lr][4 * lq], pl);
+            ChunkRec *rec = recs + (int64_t)gch * HV + h0 + v;
+            st4(&rec->TP[2][b][lr][4 * lq], ph);
+            st4(&rec->TP[3][b][lr][4 * lq], pl);
         }
     }
     __syncthreads();
 
-    // ---- stage 2: T = (I + A)^-1, block by block (T overwrites the k rows)
+    // ---- stage 2: per v-head v (waves 4 v .. 4 v + 3), T = (I + A)^-1 block
+    // by block (T overwrites the k rows)
     {
+        const int v = w >> 2, wb = w & 3;
         if (lane < 16) {
-            // diagonal block w by forward substitution; lane j owns column j
-            const Blk &Ad = sm.A[blk(w, w)];
+            // diagonal block wb by forward substitution; lane j owns column j
+            const Blk &Ad = sm.A[v][blk(wb, wb)];
             float xcol[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -360,44 +377,47 @@ __global__ __launch_bounds__(NTH) void chunk_prep_kernel(RecurrentArgs a, ChunkR
                 for (int i = 0; i < r; ++i) acc = __builtin_fmaf(-Ad[r][i], xcol[i], acc);
                 xcol[r] = acc;
             }
-            Blk &Td = sm.u.T[blk(w, w)];
+            Blk &Td = sm.u.T[v][blk(wb, wb)];
 #pragma unroll
             for (int r = 0; r < 16; ++r) Td[r][lane] = xcol[r];
         }
         __syncthreads();
-        // T_bc = -T_bb (sum_{c<=m<b} A_bm T_mc); wave c walks down column
-        // block c, so every input is its own earlier result or a diagonal block
-        const int c = w;
-        for (int b = c + 1; b < 4 && w < 3; ++b) {
+        // T_bc = -T_bb (sum_{c<=m<b} A_bm T_mc); wave c of the v-head walks
+        // down column block c, so every input is its own earlier result or a
+        // diagonal block
+        const int c = wb;
+        for (int b = c + 1; b < 4 && c < 3; ++b) {
             f32x4 m = {0.f, 0.f, 0.f, 0.f};
-            for (int mm = c; mm < b; ++mm) m = mm16(sm.A[blk(b, mm)], sm.u.T[blk(mm, c)], m, lane);
-            put16(sm.u.T[blk(b, c)], m, 1.f, lane);
+            for (int mm = c; mm < b; ++mm) m = mm16(sm.A[v][blk(b, mm)], sm.u.T[v][blk(mm, c)], m, lane);
+            put16(sm.u.T[v][blk(b, c)], m, 1.f, lane);
             f32x4 t = {0.f, 0.f, 0.f, 0.f};
-            t = mm16(sm.u.T[blk(b, b)], sm.u.T[blk(b, c)], t, lane);
-            put16(sm.u.T[blk(b, c)], t, -1.f, lane);
+            t = mm16(sm.u.T[v][blk(b, b)], sm.u.T[v][blk(b, c)], t, lane);
+            put16(sm.u.T[v][blk(b, c)], t, -1.f, lane);
         }
         __syncthreads();
-        // hi/lo to the workspace, the ten blocks only, 8 consecutive entries per lane
+        // hi/lo to the workspace, the ten blocks of each v-head only, 8
+        // consecutive entries per lane
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int idx = tid + NTH * e;          // 320 groups of 8
-            if (idx < NBLK16 * 32) {
-                const int b = idx >> 5, r = (idx >> 1) & 15, c0 = (idx & 1) * 8;
+        for (int e = 0; e < (VPW * NBLK16 * 32 + NT - 1) / NT; ++e) {
+            const int idx = tid + NT * e;           // 320 groups of 8 per v-head
+            if (idx < VPW * NBLK16 * 32) {
+                const int vv = idx / (NBLK16 * 32), q = idx - vv * (NBLK16 * 32);
+                const int b = q >> 5, r = (q >> 1) & 15, c0 = (q & 1) * 8;
                 bf16x8 hv, lv;
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
+                for (int qq = 0; qq < 8; ++qq) {
                     __bf16 hi, lo;
-                    split(sm.u.T[b][r][c0 + q], hi, lo);
-                    hv[q] = hi;
-                    lv[q] = lo;
+                    split(sm.u.T[vv][b][r][c0 + qq], hi, lo);
+                    hv[qq] = hi;
+                    lv[qq] = lo;
                 }
+                ChunkRec *rec = recs + (int64_t)gch * HV + h0 + vv;
                 st8_stream(&rec->TP[0][b][r][c0], hv);
                 st8_stream(&rec->TP[1][b][r][c0], lv);
             }
         }
     }
 }
-
 // ---------------------------------------------------------------------------
 // scan, row-split form: one workgroup per (sequence, v-head, 16 NW v rows),
 // wave w owning 16 v rows with the whole chain of a chunk in its registers
@@ -756,7 +776,13 @@ hipError_t launch_chunk_recurrent(const RecurrentArgs &a, void *workspace, int n
     const long long scan_blocks = heads * nvb;
     if (scan_blocks == 0) return hipSuccess;
     if (prep_blocks > 0x7fffffffLL || scan_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)prep_blocks), dim3(NTH), 0, stream, a, recs, kts, (int)mc);
+    // two v-heads per prep workgroup whenever the v-heads of a q/k head pair up
+    if ((a.num_v_heads / a.num_k_heads) % 2 == 0)
+        hipLaunchKernelGGL(chunk_prep_kernel<2>, dim3((unsigned)(prep_blocks / 2)), dim3(2 * NTH), 0, stream, a, recs,
+                           kts, (int)mc);
+    else
+        hipLaunchKernelGGL(chunk_prep_kernel<1>, dim3((unsigned)prep_blocks), dim3(NTH), 0, stream, a, recs, kts,
+                           (int)mc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (wide)
