@@ -104,13 +104,10 @@ __device__ __forceinline__ void split4(const f32x4 &v, bf16x4 &hi, bf16x4 &lo) {
 
 __device__ __forceinline__ void st4(__bf16 *p, const bf16x4 &v) { *reinterpret_cast<bf16x4 *>(p) = v; }
 
-// Full-line workspace stores (T, K^T) and the final state are streaming
-// (nontemporal): written once per launch, they leave no dirty lines behind
-// for the next kernel to write back.  P is written in 32-byte pieces per
-// row and stays on plain stores, which the L2 merges into whole lines.
-__device__ __forceinline__ void st8_stream(__bf16 *p, const bf16x8 &v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<bf16x8 *>(p));
-}
+// Workspace stores are plain: the scan reads the records right after the
+// prep, and finds them in the caches (streaming stores for T and K^T made
+// the whole call 2-3% slower).  The scan's final state is streaming.
+__device__ __forceinline__ void st8(__bf16 *p, const bf16x8 &v) { *reinterpret_cast<bf16x8 *>(p) = v; }
 
 // A 64 x 64 lower-triangular fp32 matrix in LDS as its ten 16 x 16 blocks
 // (b, c), b >= c, block index b (b + 1) / 2 + c; rows padded to 20 floats
@@ -311,7 +308,7 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
         for (int jj = 0; jj < TPT; ++jj) col[jj >> 3][jj & 7] = sm.u.K[TPT * part + jj][d];
         __bf16 *dst = &kts[(int64_t)gch * a.num_k_heads + hk].Kt[d][TPT * part];
 #pragma unroll
-        for (int m = 0; m < TPT / 8; ++m) st8_stream(dst + 8 * m, col[m]);
+        for (int m = 0; m < TPT / 8; ++m) st8(dst + 8 * m, col[m]);
     }
 
     // ---- stage 1: the ten lower-triangular tiles (t-tile bt, i-tile bc) of
@@ -412,8 +409,8 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
                     lv[qq] = lo;
                 }
                 ChunkRec *rec = recs + (int64_t)gch * HV + h0 + vv;
-                st8_stream(&rec->TP[0][b][r][c0], hv);
-                st8_stream(&rec->TP[1][b][r][c0], lv);
+                st8(&rec->TP[0][b][r][c0], hv);
+                st8(&rec->TP[1][b][r][c0], lv);
             }
         }
     }
