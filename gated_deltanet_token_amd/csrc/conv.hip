@@ -81,9 +81,10 @@ __global__ __launch_bounds__(THREADS) void conv_varlen_kernel(
 #pragma unroll
     for (int i = 0; i < 3; ++i) h[i] = make_uint4(h[i].x & keep, h[i].y & keep, h[i].z & keep, h[i].w & keep);
 
-    // Output rows, streamed out (written once, not read again by this
-    // launch).  Window row j is h[j] for j < 3, else r[j - 3]; pair j holds
-    // window rows (j, j + 1) and serves output rows j and j - 2.
+    // Output rows, on plain stores: the prefill path reads them right away
+    // (the chunkwise rule's q, k and v), and finds them in the caches.
+    // Window row j is h[j] for j < 3, else r[j - 3]; pair j holds window
+    // rows (j, j + 1) and serves output rows j and j - 2.
     RowPairs pr[kChunk + 2];
 #pragma unroll
     for (int j = 0; j < kChunk + 2; ++j) {
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(THREADS) void conv_varlen_kernel(
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
         const uint4 out = conv_pairs(taps, pr[i], pr[i + 2], SILU);
-        if (i < n) store_stream16(y + (int64_t)(t0 + i) * y_stride + c0, out);
+        if (i < n) *reinterpret_cast<uint4 *>(y + (int64_t)(t0 + i) * y_stride + c0) = out;
     }
 
     if (first) {

@@ -50,11 +50,6 @@ __device__ __forceinline__ uint4 load_stream16(const uint16_t *p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ void store_stream16(uint16_t *p, const uint4 &v) {
-    const u32x4 w = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
-}
-
 // unpack 8 bf16 (one 16-byte vector) into fp32
 __device__ __forceinline__ void unpack8(const uint4 &v, float *f) {
     f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
