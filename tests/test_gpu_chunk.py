@@ -57,6 +57,9 @@ def test_mixed_step_prefill_chunks():
     ([127, 0, 128, 129], 2, 2, 64, [0, 1, 1, 0], [False, False, True, False]),
     ([200, 5], 1, 2, 256, None, None),
     ([70, 33], 4, 8, 96, [1, 1], [True, False]),
+    # three v-heads per q/k head: one v-head per prep workgroup, K^T written
+    # by the first of each three
+    ([90, 40, 64], 2, 6, 64, [0, 1, 1], None),
 ])
 @pytest.mark.parametrize("scale,norm,views", [(1.0, True, False), (0.0884, True, True)])
 def test_chunk_edges(lens, HK, HV, dv_, hi, pad, scale, norm, views):
