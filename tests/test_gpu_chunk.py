@@ -157,3 +157,14 @@ def test_chunk_many_sequences():
     check_bf16(o, o_ref, "chunk many-sequence o")
     used = [int(idx[s]) for s in range(S) if lens[s] > 0 and idx[s] >= 0]
     check_state(st, st_ref, d["state"], used)
+
+
+def test_chunk_long_sequence():
+    """One 8,001-token sequence (126 chunks in series, the last holding one
+    token) next to a short one: the state is carried through every chunk
+    boundary, and chunk indices run past a hundred."""
+    lens = [8001, 37]
+    d = synth.random_gdn(37, 78, lens, 2, 4, 128, 64, num_slots=4, has_init=[1, 0])
+    o, st, o_ref, st_ref = run_chunk(d)
+    check_bf16(o, o_ref, "chunk long-sequence o")
+    check_state(st, st_ref, d["state"], [int(s) for s in d["state_indices"]])
