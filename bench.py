@@ -302,6 +302,43 @@ def cpu_baseline(seed, n_req, seq_len):
                       "rule); serial C in fp64; %.1f s" % (n_req, seq_len, elapsed)}
 
 
+def bracket_runs(kinds, kind, single_stride=1):
+    """Events that bracket maximal runs of consecutive ``kind`` launches in
+    ``kinds`` (the kind of every launch of a pass, as (step, call) -> kind
+    lists, in launch order): every run of several launches, and every
+    ``single_stride``-th run of one launch.  Returns the bracket map
+    ((step, call) -> "open" / "close" / "both"), the number of events, each
+    bracketed run's weight (1 for a long run; for the others, the number of
+    one-launch runs per bracketed one, so the weighted sum of the spans
+    estimates the kind's total time) and the number of launches inside the
+    bracketed runs.  Kernels on one stream run back to back, so a run's span
+    is the sum of its kernels' durations plus the (sub-microsecond) dispatch
+    gaps between them."""
+    runs, cur = [], None
+    for si, step in enumerate(kinds):
+        for ci, k in enumerate(step):
+            if k == kind:
+                if cur is None:
+                    cur = []
+                    runs.append(cur)
+                cur.append((si, ci))
+            else:
+                cur = None
+    singles = [r for r in runs if len(r) == 1]
+    picked_singles = singles[::single_stride]
+    w_single = len(singles) / max(len(picked_singles), 1)
+    keep = {id(r) for r in picked_singles}
+    picked = [r for r in runs if len(r) > 1 or id(r) in keep]
+    br = {}
+    for run in picked:
+        if len(run) == 1:
+            br[run[0]] = "both"
+        else:
+            br[run[0]], br[run[-1]] = "open", "close"
+    weights = [1.0 if len(r) > 1 else w_single for r in picked]
+    return br, 2 * len(picked), weights, sum(len(r) for r in picked)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -466,39 +503,7 @@ def main():
                     ev += 1
         return ev
 
-    def bracket_runs(kind, single_stride=1):
-        """Events that bracket maximal runs of consecutive ``kind`` launches
-        (in launch order): every run of several launches, and every
-        ``single_stride``-th run of one launch.  Returns the bracket map, the
-        number of events, each bracketed run's weight (1 for a long run, the
-        number of one-launch runs per bracketed one for the others, so the
-        weighted sum of the spans estimates the kind's total time) and the
-        number of launches inside the bracketed runs.  Kernels on one stream
-        run back to back, so a run's span is the sum of its kernels' durations
-        plus the (sub-microsecond) dispatch gaps between them."""
-        runs, cur = [], None
-        for si, calls in enumerate(plans):
-            for ci, c in enumerate(calls):
-                if c[0] == kind:
-                    if cur is None:
-                        cur = []
-                        runs.append(cur)
-                    cur.append((si, ci))
-                else:
-                    cur = None
-        singles = [r for r in runs if len(r) == 1]
-        picked_singles = singles[::single_stride]
-        w_single = len(singles) / max(len(picked_singles), 1)
-        keep = {id(r) for r in picked_singles}
-        picked = [r for r in runs if len(r) > 1 or id(r) in keep]
-        br = {}
-        for run in picked:
-            if len(run) == 1:
-                br[run[0]] = "both"
-            else:
-                br[run[0]], br[run[-1]] = "open", "close"
-        weights = [1.0 if len(r) > 1 else w_single for r in picked]
-        return br, 2 * len(picked), weights, sum(len(r) for r in picked)
+    plan_kinds = [[c[0] for c in calls] for calls in plans]
 
     def span_ms(events, weights):
         return sum(w * events[2 * i].elapsed_time(events[2 * i + 1]) for i, w in enumerate(weights))
@@ -515,7 +520,7 @@ def main():
     torch.cuda.synchronize()
     kern = {}
     for k in kinds:
-        br, n_ev, wts, _ = bracket_runs(k)
+        br, n_ev, wts, _ = bracket_runs(plan_kinds, k)
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
         run_pass((br, evs))
         torch.cuda.synchronize()
@@ -533,7 +538,7 @@ def main():
     # (weighted), a stratified estimate of its total time.  Each recorded
     # event idles the stream for ~5 us on this GPU: bracketing all ~280 runs
     # of a pass cost ~2% of the measured throughput.
-    br, n_ev, wts, n_timed = bracket_runs(dominant, ROOFLINE_STRIDE)
+    br, n_ev, wts, n_timed = bracket_runs(plan_kinds, dominant, ROOFLINE_STRIDE)
     live = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()

@@ -59,3 +59,26 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=60)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+def test_bracket_runs_stratified_sample(bench):
+    # a pass: a run of three F launches, ten one-launch runs of F (each
+    # followed by another kind), then another run of three
+    kinds = [["F", "F"], ["F", "C"]] + [["F", "R"] for _ in range(10)] + [["C", "F", "F", "F"]]
+    br, n_ev, w, n_timed = bench.bracket_runs(kinds, "F", 1)
+    assert n_ev == 2 * 12 and w == [1.0] * 12 and n_timed == 3 + 10 + 3
+    assert br[(0, 0)] == "open" and br[(1, 0)] == "close"
+    assert br[(12, 1)] == "open" and br[(12, 3)] == "close"
+    assert all(br[(s, 0)] == "both" for s in range(2, 12))
+    br, n_ev, w, n_timed = bench.bracket_runs(kinds, "F", 3)
+    # both long runs, and one-launch runs 0, 3, 6 and 9 of the ten (steps 2, 5, 8, 11)
+    assert n_ev == 2 * 6 and n_timed == 3 + 4 + 3
+    assert sorted(k for k, v in br.items() if v == "both") == [(2, 0), (5, 0), (8, 0), (11, 0)]
+    assert w == [1.0, 2.5, 2.5, 2.5, 2.5, 1.0]
+    # with equal launch durations the weighted spans give the exact total
+    d = 7.0
+    spans = [3 * d, d, d, d, d, 3 * d]
+    assert sum(x * y for x, y in zip(w, spans)) == pytest.approx(16 * d)
+    # events come in launch order: opens and closes alternate
+    flat = [e for k in sorted(br) for e in (("open", "close") if br[k] == "both" else (br[k],))]
+    assert flat == ["open", "close"] * 6
