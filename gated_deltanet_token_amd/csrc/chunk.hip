@@ -40,7 +40,6 @@ constexpr int CT = 64;          // tokens per chunk
 constexpr int DKC = 128;        // head_k_dim
 constexpr int NTH = 256;        // 4 waves
 constexpr int LDK = DKC + 8;    // padded LDS row (bf16) of a [*][128] tile
-constexpr int LDT = CT + 8;     // padded LDS row (bf16) of a [*][64] tile
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -211,8 +210,7 @@ struct PrepSmem {
 };
 
 template <int VPW>
-__global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, ChunkRec *recs, KtRec *kts,
-                                                              int max_chunks) {
+__global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, ChunkRec *recs, KtRec *kts) {
     constexpr int NT = NTH * VPW, NW = NT / 64;
     __shared__ PrepSmem<VPW> sm;
     const int HV = a.num_v_heads, NP = HV / VPW;
@@ -776,10 +774,9 @@ hipError_t launch_chunk_recurrent(const RecurrentArgs &a, void *workspace, int n
     // two v-heads per prep workgroup whenever the v-heads of a q/k head pair up
     if ((a.num_v_heads / a.num_k_heads) % 2 == 0)
         hipLaunchKernelGGL(chunk_prep_kernel<2>, dim3((unsigned)(prep_blocks / 2)), dim3(2 * NTH), 0, stream, a, recs,
-                           kts, (int)mc);
+                           kts);
     else
-        hipLaunchKernelGGL(chunk_prep_kernel<1>, dim3((unsigned)prep_blocks), dim3(NTH), 0, stream, a, recs, kts,
-                           (int)mc);
+        hipLaunchKernelGGL(chunk_prep_kernel<1>, dim3((unsigned)prep_blocks), dim3(NTH), 0, stream, a, recs, kts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (wide)
