@@ -12,10 +12,10 @@
 //   S_C  = G_C S0 + sum_i exp(L_C - L_i) u_i kh_i^T
 //
 // Two launches:
-//  * prep (one workgroup per (chunk, v-head), all chunks in parallel): the
-//    parts that do not depend on the state -- norms, cumulative decay,
-//    T = (I + A)^-1, P_ti = scale exp(L_t - L_i)(qh_t . kh_i) (i <= t), K^T
-//    -- written to the caller's workspace;
+//  * prep (one workgroup per (chunk, one or two v-heads of a q/k head), all
+//    chunks in parallel): the parts that do not depend on the state --
+//    norms, cumulative decay, T = (I + A)^-1, P_ti = scale exp(L_t - L_i)
+//    (qh_t . kh_i) (i <= t), K^T -- written to the caller's workspace;
 //  * scan (one workgroup per (sequence, v-head, 32 or 64 v rows), serial
 //    over the sequence's chunks, each wave owning 16 v rows): [K;Q] S0^T,
 //    R, U = T R, o = S0 part + P U and S_C^T = G_C S0^T + K^T U', with the
@@ -428,7 +428,7 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
 // elements (4 (l / 16) + i, l % 16), i < 4, so two tiles stacked along the
 // contraction index give lane l the contraction positions 4 (l / 16) + i and
 // 16 + 4 (l / 16) + i of a 32-wide block.  The shared A side is read from LDS
-// with the same positions (two 8-byte pieces per fragment), so no
+// with the same positions (one 16-byte read per fragment, below), so no
 // accumulator ever goes through LDS and no barrier separates the phases.
 // The waves meet twice per chunk, to restage the next chunk's operands
 // (prefetched into registers while the current chunk runs).
@@ -437,8 +437,8 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
 // + 3 and 16 + 4 g .. 16 + 4 g + 3) sit side by side at 8 g .. 8 g + 7: a
 // fragment is one aligned 16-byte read.  Column c of a block is stored at
 // 8 ((c % 16) / 4) + 4 (c / 16) + c % 4; eight consecutive columns 8 h .. 8 h
-// + 7 (h < 4) therefore land as two 4-column halves at pstart(h) and
-// pstart(h) + 8.  Rows padded by 8 bf16 (16 bytes): eight consecutive rows
+// + 7 (h < 4) therefore land as two 4-column halves at pstart(8 h) and
+// pstart(8 h) + 8.  Rows padded by 8 bf16 (16 bytes): eight consecutive rows
 // of a 16-byte fragment read then fall on eight different 16-byte bank
 // groups (row pitch = 16 mod 128 bytes).
 constexpr int RLDK = DKC + 8;
