@@ -155,10 +155,14 @@ int check_recurrent(const gdn_bf16 *q, int64_t q_stride, const gdn_bf16 *k, int6
     if (!query_start_loc && num_tokens != num_seqs)
         return fail(GDN_ERR_INVALID, "without query_start_loc num_tokens must equal num_seqs");
     const Span os = row_span(o, num_tokens, o_stride, v_w, 2);
+    const Span st = {(uintptr_t)state, (uintptr_t)state + (uintptr_t)num_slots * (uintptr_t)v_w * head_k_dim * 4};
+    const Span gs = {(uintptr_t)g, (uintptr_t)g + (uintptr_t)num_tokens * num_v_heads * 4};
+    const Span bs = {(uintptr_t)beta, (uintptr_t)beta + (uintptr_t)num_tokens * num_v_heads * 4};
     if (overlap(os, row_span(q, num_tokens, q_stride, qk_w, 2)) ||
         overlap(os, row_span(k, num_tokens, k_stride, qk_w, 2)) ||
-        overlap(os, row_span(v, num_tokens, v_stride, v_w, 2)))
-        return fail(GDN_ERR_INVALID, "o overlaps q, k or v");
+        overlap(os, row_span(v, num_tokens, v_stride, v_w, 2)) || overlap(os, st) || overlap(os, gs) ||
+        overlap(os, bs))
+        return fail(GDN_ERR_INVALID, "o overlaps q, k, v, g, beta or state");
     if (num_seqs == 0 || num_tokens == 0) {
         ok();
         return 1;
@@ -218,6 +222,17 @@ GDN_EXPORT int gdn_chunk_gated_delta_rule(const gdn_bf16 *q, int64_t q_stride, c
     if (((uintptr_t)workspace & 255u) != 0) return fail(GDN_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
     if (workspace_bytes < need)
         return fail(GDN_ERR_CAPACITY, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    // the kernels write the first `need` bytes of the workspace: they must not
+    // be any operand's
+    const Span ws = {(uintptr_t)workspace, (uintptr_t)workspace + need};
+    const int64_t qk_w = (int64_t)num_k_heads * head_k_dim, v_w = (int64_t)num_v_heads * head_v_dim;
+    const Span st = {(uintptr_t)state, (uintptr_t)state + (uintptr_t)num_slots * (uintptr_t)v_w * head_k_dim * 4};
+    const Span gs = {(uintptr_t)g, (uintptr_t)g + (uintptr_t)num_tokens * num_v_heads * 4};
+    const Span bs = {(uintptr_t)beta, (uintptr_t)beta + (uintptr_t)num_tokens * num_v_heads * 4};
+    if (overlap(ws, row_span(q, num_tokens, q_stride, qk_w, 2)) || overlap(ws, row_span(k, num_tokens, k_stride, qk_w, 2)) ||
+        overlap(ws, row_span(v, num_tokens, v_stride, v_w, 2)) || overlap(ws, row_span(o, num_tokens, o_stride, v_w, 2)) ||
+        overlap(ws, st) || overlap(ws, gs) || overlap(ws, bs))
+        return fail(GDN_ERR_INVALID, "workspace overlaps q, k, v, g, beta, state or o");
     return hip_status(gdn::launch_chunk_recurrent(a, workspace, num_tokens, (hipStream_t)stream),
                       "chunk recurrent launch");
 }

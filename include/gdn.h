@@ -201,7 +201,7 @@ int gdn_causal_conv1d_update(const gdn_bf16 *x, int64_t x_stride,
  *
  * Errors: GDN_ERR_INVALID (required pointer NULL, negative count,
  * num_v_heads % num_k_heads, strides too small, num_tokens != num_seqs
- * without query_start_loc, o overlapping q/k/v); GDN_ERR_UNSUPPORTED
+ * without query_start_loc, o overlapping q/k/v/g/beta/state); GDN_ERR_UNSUPPORTED
  * (head_k_dim not in {16, 32, 64, 128}, head_v_dim not a positive multiple
  * of 8 up to 256, alignment contract); GDN_ERR_HIP.
  */
@@ -248,7 +248,9 @@ int gdn_fused_recurrent_decode(const gdn_bf16 *q, int64_t q_stride,
  *                    num_k_heads, num_v_heads) bytes; its contents on entry
  *                    do not matter and are overwritten.  Calls that share a
  *                    workspace must not overlap in time.
- * Errors beyond those: GDN_ERR_INVALID (NULL workspace), GDN_ERR_UNSUPPORTED
+ * Errors beyond those: GDN_ERR_INVALID (NULL workspace, or a workspace
+ * whose first gdn_chunk_workspace_size bytes overlap q, k, v, g, beta,
+ * state or o), GDN_ERR_UNSUPPORTED
  * (misaligned workspace, a token stride of 2^24 elements or more),
  * GDN_ERR_CAPACITY (workspace_bytes too small).
  * Results equal the per-token recurrence up to fp32 rounding (a different

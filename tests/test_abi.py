@@ -117,7 +117,8 @@ def test_conv_update_validation(kw, code):
     assert update(**kw) == code, gdn.lib.gdn_last_error()
 
 
-Q, K_, V, G, BE, ST, O = (A + i * 0x4000000 for i in range(7))
+# 256 MiB apart, after the conv buffers: the 64-slot state pool alone spans 128 MiB
+Q, K_, V, G, BE, ST, O = (A + (i + 1) * 0x10000000 for i in range(7))
 
 
 def rec(**kw):
@@ -137,6 +138,7 @@ def rec(**kw):
     (dict(qs=2000), INV), (dict(vs=4000), INV), (dict(os=1024), INV),
     (dict(T=33), INV),                           # one token per sequence without qsl
     (dict(o=V), INV),                            # o overlaps v
+    (dict(o=ST + 0x10000), INV), (dict(o=G), INV), (dict(o=BE), INV),   # o over the state, g, beta
     (dict(dk=96), UNS), (dict(dk=256), UNS), (dict(dv=100), UNS), (dict(dv=512), UNS),
     (dict(qs=2052), UNS), (dict(q=Q + 8), UNS), (dict(st=ST + 4), UNS),
 ])
@@ -151,7 +153,7 @@ def test_error_text_cleared_on_success():
     assert gdn.lib.gdn_last_error() == b""
 
 
-WS = A + 0x40000000
+WS = A + 0x80000000
 WS_NEED = gdn.gdn_chunk_workspace_size(3, 2019, 16, 32)
 
 
@@ -171,6 +173,8 @@ def chunk(**kw):
     (dict(dk=64), UNS), (dict(dk=16), UNS), (dict(dv=48), UNS), (dict(dv=512), UNS), (dict(q=Q + 8), UNS),
     (dict(ws=None), INV), (dict(ws=WS + 128), UNS), (dict(wsb=WS_NEED - 1), CAP),
     (dict(os=1 << 24), UNS),     # 32-bit byte offsets within a 64-token chunk
+    # a workspace over an operand: o, the state pool, q
+    (dict(ws=O), INV), (dict(ws=ST + 0x100000), INV), (dict(ws=Q), INV),
 ])
 def test_chunk_validation(kw, code):
     assert chunk(**kw) == code, gdn.lib.gdn_last_error()
