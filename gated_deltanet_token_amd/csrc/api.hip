@@ -59,8 +59,13 @@ int check_conv_common(const void *x, int64_t x_stride, const void *weight, const
     if (!aligned16(x) || !aligned16(y) || !aligned16(weight) || !aligned16(conv_state) ||
         (bias && !aligned16(bias)))
         return fail(GDN_ERR_UNSUPPORTED, "x, y, weight, bias and conv_state must be 16-byte aligned");
-    if (overlap(row_span(x, rows, x_stride, channels, 2), row_span(y, rows, y_stride, channels, 2)))
-        return fail(GDN_ERR_INVALID, "y overlaps x");
+    const Span ys = row_span(y, rows, y_stride, channels, 2);
+    if (overlap(row_span(x, rows, x_stride, channels, 2), ys)) return fail(GDN_ERR_INVALID, "y overlaps x");
+    const Span cs = {(uintptr_t)conv_state, (uintptr_t)conv_state + (uintptr_t)num_slots * 3 * channels * 2};
+    const Span ws = {(uintptr_t)weight, (uintptr_t)weight + (uintptr_t)channels * width * 2};
+    const Span bs = {(uintptr_t)bias, bias ? (uintptr_t)bias + (uintptr_t)channels * 2 : (uintptr_t)bias};
+    if (overlap(ys, cs) || overlap(ys, ws) || overlap(ys, bs))
+        return fail(GDN_ERR_INVALID, "y overlaps conv_state, weight or bias");
     return ok();
 }
 
@@ -269,11 +274,19 @@ GDN_EXPORT int gdn_fused_conv_decode(const gdn_bf16 *x, int64_t x_stride, const 
         !aligned16(state) || !aligned16(o) || (y && !aligned16(y)))
         return fail(GDN_ERR_UNSUPPORTED, "x, conv_weight, conv_bias, conv_state, state, o and y must be 16-byte aligned");
     const Span xs = row_span(x, batch, x_stride, channels, 2);
-    if (overlap(xs, row_span(o, batch, o_stride, v_w, 2)))
-        return fail(GDN_ERR_INVALID, "o overlaps x");
-    if (y && (overlap(xs, row_span(y, batch, y_stride, channels, 2)) ||
-              overlap(row_span(o, batch, o_stride, v_w, 2), row_span(y, batch, y_stride, channels, 2))))
-        return fail(GDN_ERR_INVALID, "y overlaps x or o");
+    const Span os = row_span(o, batch, o_stride, v_w, 2);
+    const Span sts = {(uintptr_t)state,
+                      (uintptr_t)state + (uintptr_t)num_slots * (uintptr_t)v_w * head_k_dim * 4};
+    const Span css = {(uintptr_t)conv_state, (uintptr_t)conv_state + (uintptr_t)num_conv_slots * 3 * channels * 2};
+    const Span gs = {(uintptr_t)g, (uintptr_t)g + (uintptr_t)batch * num_v_heads * 4};
+    const Span bes = {(uintptr_t)beta, (uintptr_t)beta + (uintptr_t)batch * num_v_heads * 4};
+    if (overlap(xs, os) || overlap(os, sts) || overlap(os, css) || overlap(os, gs) || overlap(os, bes))
+        return fail(GDN_ERR_INVALID, "o overlaps x, state, conv_state, g or beta");
+    if (y) {
+        const Span ys = row_span(y, batch, y_stride, channels, 2);
+        if (overlap(xs, ys) || overlap(os, ys) || overlap(ys, sts) || overlap(ys, css))
+            return fail(GDN_ERR_INVALID, "y overlaps x, o, state or conv_state");
+    }
     if (batch == 0) return ok();
     gdn::FusedDecodeArgs a{x, x_stride, conv_weight, conv_bias, conv_state, (int)channels, g, beta, state,
                            state_indices, o, o_stride, y, y_stride, batch, num_k_heads, num_v_heads, head_k_dim,

@@ -124,11 +124,12 @@ int gdn_build_conv_chunks(const int32_t *qsl_host, int32_t num_seqs,
  *   chunks, n_chunks  descriptors from gdn_build_conv_chunks on the same
  *                     query_start_loc, copied to the device.  Both NULL/0 is a
  *                     valid empty call; exactly one of them set is an error.
- *   y                 bf16 [num_tokens][y_stride]; must not overlap x
+ *   y                 bf16 [num_tokens][y_stride]; must not overlap x,
+ *                     conv_state, weight or bias
  *
  * Errors: GDN_ERR_INVALID (required pointer NULL, negative count,
- * (chunks == NULL) != (n_chunks == 0), stride < channels, x and y overlap,
- * num_slots < 1); GDN_ERR_UNSUPPORTED (width != 4, channels % 8, strides or
+ * (chunks == NULL) != (n_chunks == 0), stride < channels, y overlapping x,
+ * conv_state, weight or bias, num_slots < 1); GDN_ERR_UNSUPPORTED (width != 4, channels % 8, strides or
  * pointers off the 16-byte contract); GDN_ERR_HIP (launch failure).
  */
 int gdn_causal_conv1d_varlen(const gdn_bf16 *x, int64_t x_stride,
@@ -305,7 +306,8 @@ int gdn_chunk_gated_delta_rule(const gdn_bf16 *q, int64_t q_stride,
  *
  * Errors: GDN_ERR_INVALID (required pointer NULL, negative batch, slot
  * counts < 1, num_v_heads % num_k_heads, strides too small, o or y
- * overlapping x, y overlapping o); GDN_ERR_UNSUPPORTED (head dims as for
+ * overlapping x, state or conv_state, o overlapping g or beta, y
+ * overlapping o); GDN_ERR_UNSUPPORTED (head dims as for
  * gdn_fused_recurrent_decode, more than 8192 conv channels read by one q/k
  * head group, alignment contract); GDN_ERR_HIP.
  */

@@ -93,6 +93,7 @@ def varlen(**kw):
     (dict(nch=0), INV),                          # pair mismatch: buffer without count
     (dict(nch=-1), INV), (dict(S=-1), INV), (dict(T=-1), INV), (dict(slots=0), INV),
     (dict(xs=8000), INV), (dict(ys=100), INV), (dict(y=X), INV), (dict(y=X + 2 * 8192), INV),
+    (dict(y=CS), INV), (dict(y=W, x=Y), INV), (dict(y=B), INV),     # y over conv_state, weight, bias
     (dict(nch=3000), INV), (dict(S=0), INV),
     (dict(K=3), UNS), (dict(K=5), UNS), (dict(C=8190, xs=8190, ys=8190), UNS),
     (dict(xs=8196), UNS), (dict(x=X + 2), UNS), (dict(b=B + 8), UNS), (dict(cs=CS + 4), UNS),
@@ -110,7 +111,7 @@ def update(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(x=None), INV), (dict(idx=None), INV), (dict(B=-1), INV), (dict(y=X), INV),
+    (dict(x=None), INV), (dict(idx=None), INV), (dict(B=-1), INV), (dict(y=X), INV), (dict(y=CS), INV),
     (dict(slots=0), INV), (dict(K=2), UNS), (dict(C=12, xs=16, ys=16), UNS), (dict(y=Y + 6), UNS),
 ])
 def test_conv_update_validation(kw, code):
@@ -204,6 +205,8 @@ def fused(**kw):
     (dict(idx=None), INV), (dict(o=None), INV), (dict(B=-1), INV), (dict(cslots=0), INV), (dict(slots=0), INV),
     (dict(HV=24), INV), (dict(xs=8000), INV), (dict(os=1000), INV), (dict(o=X), INV),
     (dict(y=Y, ys=100), INV), (dict(y=X, ys=8192), INV),
+    (dict(o=ST), INV), (dict(o=CS), INV), (dict(o=G), INV), (dict(o=BE), INV),
+    (dict(y=CS, ys=8192), INV), (dict(y=ST, ys=8192), INV),
     (dict(dk=96), UNS), (dict(dv=12), UNS), (dict(xs=8196), UNS), (dict(x=X + 4), UNS), (dict(y=Y + 2, ys=8192), UNS),
     (dict(HK=1, HV=64, dk=128, dv=128, xs=8448), UNS),   # one q/k group reads > 8192 channels
 ])
