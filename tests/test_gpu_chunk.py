@@ -60,6 +60,9 @@ def test_mixed_step_prefill_chunks():
     # three v-heads per q/k head: one v-head per prep workgroup, K^T written
     # by the first of each three
     ([90, 40, 64], 2, 6, 64, [0, 1, 1], None),
+    # four v-heads per q/k head: two pair workgroups per q/k head, K^T written
+    # by the first
+    ([129, 64, 3], 2, 8, 64, [1, 0, 1], [False, True, False]),
 ])
 @pytest.mark.parametrize("scale,norm,views", [(1.0, True, False), (0.0884, True, True)])
 def test_chunk_edges(lens, HK, HV, dv_, hi, pad, scale, norm, views):
