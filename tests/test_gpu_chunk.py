@@ -171,3 +171,14 @@ def test_chunk_long_sequence():
     o, st, o_ref, st_ref = run_chunk(d)
     check_bf16(o, o_ref, "chunk long-sequence o")
     check_state(st, st_ref, d["state"], [int(s) for s in d["state_indices"]])
+
+
+def test_chunk_many_short_sequences_several_rounds():
+    """32 sequences of 64 tokens at the c32 head shape (2,048 tokens): 2,048
+    scan workgroups, several rounds on 256 CUs, and 1,024 prep workgroups."""
+    lens = [64] * 32
+    hi = [i % 2 == 0 for i in range(32)]
+    d = synth.random_gdn(38, 79, lens, 16, 32, 128, 128, num_slots=64, has_init=hi)
+    o, st, o_ref, st_ref = run_chunk(d)
+    check_bf16(o, o_ref, "chunk 32 x 64 o")
+    check_state(st, st_ref, d["state"], [int(s) for s in d["state_indices"]])

@@ -62,6 +62,7 @@ CASES = [
     (5, 2, 2, 16, 16, 8, (3,)),              # tiny chained geometry: 96 channels
     (7, 1, 4, 64, 72, 9, (0, 6)),            # GQA 1:4, ragged dv
     (3, 4, 8, 32, 256, 4, ()),
+    (64, 16, 32, 128, 128, 64, ()),          # every slot of the 64-slot pool
 ]
 
 
