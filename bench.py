@@ -11,11 +11,15 @@ in the 256 MB Infinity Cache, as in a model with several GDN layers.
 
 Per engine step: the host builds the exact (sequence, 8-token chunk)
 descriptors once (gdn_build_conv_chunks) and uploads them once; then for every
-layer: one fused launch for the decode rows (conv update + gated delta rule,
-gdn_fused_conv_decode), the varlen conv for the prefill rows and the
+layer: the varlen conv for the prefill rows, and the recurrence -- the
 chunkwise (matrix-core) form of the rule for the prefill chunks (q, k, v are
-column views of the conv output).  Inputs are resident in HBM before the
-timed region; every call goes through the C ABI on torch's current stream.
+column views of the conv output) and, for the decode rows, the conv update
+fused with the rule.  A step with only decode rows makes one
+gdn_fused_conv_decode call per layer, a step with only prefill rows a
+gdn_chunk_gated_delta_rule call, a step with both one
+gdn_chunk_rule_and_fused_decode call (the chunkwise scan and the decode in
+one grid).  Inputs are resident in HBM before the timed region; every call
+goes through the C ABI on torch's current stream.
 
 Output: one JSON line.  ``value`` is GDN-layer tokens per second (tokens x
 layers / wall time).  ``roofline`` is for the kernel with the largest share
@@ -115,9 +119,12 @@ def flops_recurrent(tokens):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c32_trace_4layers.md")
 _CSRC = os.path.join(ROOT, "gated_deltanet_token_amd", "csrc")
 KERNEL_SOURCES = {
-    "fused_decode": ["fused.hip", "conv_math.h", "gdr_math.h", "gdn_device.h", "gdn_internal.h"],
+    "fused_decode": ["fused.hip", "fused_unit.h", "conv_math.h", "gdr_math.h", "gdn_device.h", "gdn_internal.h"],
     "conv_varlen": ["conv.hip", "conv_math.h", "gdn_device.h", "gdn_internal.h"],
-    "recurrent_chunk": ["chunk.hip", "gdn_device.h", "gdn_internal.h"],
+    "recurrent_chunk": ["chunk.hip", "fused_unit.h", "conv_math.h", "gdr_math.h", "gdn_device.h",
+                        "gdn_internal.h"],
+    "chunk_and_decode": ["chunk.hip", "fused_unit.h", "conv_math.h", "gdr_math.h", "gdn_device.h",
+                         "gdn_internal.h"],
 }
 
 
@@ -276,7 +283,38 @@ def isolated(seed, reps=64):
                                          % "+".join(str(x) for x in lens),
                                    buffer_sets=len(sets), tokens_per_s=T3 / us * 1e6,
                                    bound="latency (serial over 64-token chunks)")
-    del sets, calls, pools
+
+    # the mixed step's recurrence as one call (gdn_chunk_rule_and_fused_decode):
+    # the same prefill chunks and 29 decode rows on other slots of the same pool,
+    # against the chunkwise call followed by the fused decode
+    nd = 29
+    didx = i32(np.random.default_rng(seed + 1).permutation(np.setdiff1d(np.arange(SLOTS), [5, 33, 60]))[:nd])
+    gd, bd = g[:nd].contiguous(), beta[:nd].contiguous()
+    msets = [(y, st, o, p) for (y, st, o), p in zip(sets, pools[:4])]
+    mixed = [lambda y=y, st=st, o=o, p=p: check(lib.gdn_chunk_rule_and_fused_decode(
+        y.data_ptr(), C, y.data_ptr() + HK * D * 2, C, y.data_ptr() + 2 * HK * D * 2, C, g3.data_ptr(),
+        b3.data_ptr(), qsl3.data_ptr(), idx3.data_ptr(), hi3.data_ptr(), o.data_ptr(), HV * D, 3, T3,
+        ws.data_ptr(), ws_bytes, p["x"].data_ptr(), C, w.data_ptr(), b.data_ptr(), p["cs"].data_ptr(), SLOTS,
+        gd.data_ptr(), bd.data_ptr(), didx.data_ptr(), p["o"].data_ptr(), HV * D, None, 0, nd, 1,
+        st.data_ptr(), SLOTS, HK, HV, D, D, f1, 1, sptr), "chunk_and_decode") for y, st, o, p in msets]
+
+    def two(y, st, o, p):
+        check(lib.gdn_chunk_gated_delta_rule(
+            y.data_ptr(), C, y.data_ptr() + HK * D * 2, C, y.data_ptr() + 2 * HK * D * 2, C, g3.data_ptr(),
+            b3.data_ptr(), st.data_ptr(), SLOTS, qsl3.data_ptr(), idx3.data_ptr(), hi3.data_ptr(), o.data_ptr(),
+            HV * D, 3, T3, HK, HV, D, D, ws.data_ptr(), ws_bytes, f1, 1, sptr), "recurrent_chunk")
+        check(lib.gdn_fused_conv_decode(
+            p["x"].data_ptr(), C, w.data_ptr(), b.data_ptr(), p["cs"].data_ptr(), SLOTS, gd.data_ptr(),
+            bd.data_ptr(), st.data_ptr(), SLOTS, didx.data_ptr(), p["o"].data_ptr(), HV * D, None, 0, nd, HK, HV,
+            D, D, 1, f1, 1, sptr), "fused_decode")
+    us_two = timed([lambda m=m: two(*m) for m in msets])
+    us = timed(mixed)
+    out["chunk_and_decode"] = entry(us, bytes_recurrent(T3, 1, 3) + bytes_fused_decode(nd),
+                                    flops_recurrent(T3) + flops_recurrent(nd),
+                                    shape="the mixed step's recurrence: 3 prefill chunks of %s tokens and %d "
+                                          "decode rows (conv update + rule)" % ("+".join(str(x) for x in lens), nd),
+                                    buffer_sets=len(msets), two_calls_us=us_two)
+    del sets, msets, calls, mixed, pools
     torch.cuda.synchronize()
     return out
 
@@ -437,9 +475,9 @@ def main():
             X, Y, O = ly["x"].data_ptr(), ly["y"].data_ptr(), ly["o"].data_ptr()
             G, B = ly["g"].data_ptr(), ly["beta"].data_ptr()
             yq, yk, yv = Y, Y + HK * D * 2, Y + 2 * HK * D * 2
-            if nd:
+            di = dec_idx_d.data_ptr() + int(dec_off[si]) * i32
+            if nd and not npf:
                 # decode rows: conv update fused with the recurrence (one launch)
-                di = dec_idx_d.data_ptr() + int(dec_off[si]) * i32
                 calls.append(("fused_decode", lib.gdn_fused_conv_decode,
                               (X + off * C * 2, C, ly["w"].data_ptr(), ly["b"].data_ptr(), ly["cs"].data_ptr(),
                                SLOTS, G + off * HV * 4, B + off * HV * 4, ly["state"].data_ptr(), SLOTS, di,
@@ -457,7 +495,20 @@ def main():
                                ly["cs"].data_ptr(), SLOTS, qd, pi, ph, cd, n_chunks[si], Y + nd * C * 2, C,
                                npf, tp, C, K, 1, sptr),
                               bytes_conv_varlen(tp, npf, n_init, n_chunks[si]), 0.0))
-            if npf:
+            if npf and nd:
+                # the prefill chunks' recurrence and the decode rows (conv update
+                # + recurrence) in one call, after the prefill conv
+                po = off + nd
+                calls.append(("chunk_and_decode", lib.gdn_chunk_rule_and_fused_decode,
+                              (yq + nd * C * 2, C, yk + nd * C * 2, C, yv + nd * C * 2, C, G + po * HV * 4,
+                               B + po * HV * 4, qd, pi, ph, O + po * HV * D * 2, HV * D, npf, tp, ws.data_ptr(),
+                               ws_bytes, X + off * C * 2, C, ly["w"].data_ptr(), ly["b"].data_ptr(),
+                               ly["cs"].data_ptr(), SLOTS, G + off * HV * 4, B + off * HV * 4, di,
+                               O + off * HV * D * 2, HV * D, None, 0, nd, 1, ly["state"].data_ptr(), SLOTS,
+                               HK, HV, D, D, ctypes.c_float(1.0), 1, sptr),
+                              bytes_recurrent(tp, n_init, npf) + bytes_fused_decode(nd),
+                              flops_recurrent(tp) + flops_recurrent(nd)))
+            elif npf:
                 po = off + nd
                 calls.append(("recurrent_chunk", lib.gdn_chunk_gated_delta_rule,
                               (yq + nd * C * 2, C, yk + nd * C * 2, C, yv + nd * C * 2, C, G + po * HV * 4,
@@ -512,7 +563,8 @@ def main():
         calls_of = [c for calls in plans for c in calls if c[0] == kind]
         return len(calls_of), sum(c[3] for c in calls_of), sum(c[4] for c in calls_of)
 
-    kinds = ["conv_varlen", "fused_decode", "recurrent_chunk"]
+    kinds = [k for k in ("conv_varlen", "fused_decode", "recurrent_chunk", "chunk_and_decode")
+             if any(k in ks for ks in plan_kinds)]
 
     # ---- warm-up, then one instrumented pass (untimed) for the per-kernel shares
     for _ in range(args.warmup):

@@ -27,7 +27,7 @@ CONV_WIDTH = 4
 # every entry point declared in include/gdn.h
 EXPORTS = ("gdn_last_error", "gdn_build_conv_chunks", "gdn_causal_conv1d_varlen",
            "gdn_causal_conv1d_update", "gdn_fused_recurrent_decode", "gdn_chunk_gated_delta_rule",
-           "gdn_fused_conv_decode", "gdn_chunk_workspace_size")
+           "gdn_fused_conv_decode", "gdn_chunk_workspace_size", "gdn_chunk_rule_and_fused_decode")
 
 
 class GDNError(RuntimeError):
@@ -54,6 +54,10 @@ def _bind(path):
             getattr(lib, name).restype = ctypes.c_int
     lib.gdn_fused_conv_decode.argtypes = [P, i64, P, P, P, i32, P, P, P, i32, P, P, i64, P, i64,
                                           i32, i32, i32, i32, i32, i32, f32, i32, P]
+    lib.gdn_chunk_rule_and_fused_decode.argtypes = [
+        P, i64, P, i64, P, i64, P, P, P, P, P, P, i64, i32, i32, P, ctypes.c_size_t,   # prefill tokens
+        P, i64, P, P, P, i32, P, P, P, P, i64, P, i64, i32, i32,                       # decode rows
+        P, i32, i32, i32, i32, i32, f32, i32, P]                                       # shared
     lib.gdn_chunk_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.gdn_chunk_workspace_size.restype = ctypes.c_size_t
     return lib
@@ -260,3 +264,43 @@ def gdn_fused_conv_decode(x, conv_weight, conv_bias, conv_state, g, beta, state,
         _ptr(y), 0 if y is None else _rows(y, "y"), B, num_k_heads, HV, head_k_dim, dv, int(bool(silu)),
         float(scale), int(bool(qk_l2norm)), _stream(stream))
     _check(rc, "gdn_fused_conv_decode")
+
+
+def gdn_chunk_rule_and_fused_decode(q, k, v, g, beta, state_indices, o, query_start_loc, has_initial_state,
+                                    dec_x, conv_weight, conv_bias, conv_state, dec_g, dec_beta,
+                                    dec_state_indices, dec_o, state, num_k_heads, dec_y=None, silu=True,
+                                    scale=1.0, qk_l2norm=True, stream=None, workspace=None):
+    """One engine step's recurrence on both kinds of rows: the chunkwise rule
+    over the prefill tokens (q, k, v, g, beta, o, query_start_loc, ...; as
+    gdn_chunk_gated_delta_rule) and the fused conv update + rule on the
+    decode rows (dec_*; as gdn_fused_conv_decode), sharing the state pool
+    ``state`` on distinct slots; see gdn.h."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dec_x, "dec_x"), (conv_weight, "conv_weight"),
+                 (conv_bias, "conv_bias"), (conv_state, "conv_state"), (dec_o, "dec_o"), (dec_y, "dec_y")):
+        _dtype(t, torch.bfloat16, n)
+    for t, n in ((g, "g"), (beta, "beta"), (dec_g, "dec_g"), (dec_beta, "dec_beta"), (state, "state")):
+        _dtype(t, torch.float32, n)
+    for t, n in ((state_indices, "state_indices"), (query_start_loc, "query_start_loc"),
+                 (dec_state_indices, "dec_state_indices")):
+        _dtype(t, torch.int32, n)
+    _dtype(has_initial_state, torch.uint8, "has_initial_state")
+    if not all(t.is_contiguous() for t in (g, beta, dec_g, dec_beta, state)):
+        raise ValueError("g, beta, dec_g, dec_beta and state must be contiguous")
+    T, HK, dk = q.shape
+    HV, dv = v.shape[1], v.shape[2]
+    S = state_indices.numel()
+    B = dec_x.shape[0]
+    need = gdn_chunk_workspace_size(S, T, HK, HV)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rc = lib.gdn_chunk_rule_and_fused_decode(
+        _ptr(q), _heads(q, "q"), _ptr(k), _heads(k, "k"), _ptr(v), _heads(v, "v"), _ptr(g), _ptr(beta),
+        _ptr(query_start_loc), _ptr(state_indices), _ptr(has_initial_state), _ptr(o), _heads(o, "o"), S, T,
+        _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(dec_x), _rows(dec_x, "dec_x"), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state),
+        conv_state.shape[0], _ptr(dec_g), _ptr(dec_beta), _ptr(dec_state_indices), _ptr(dec_o),
+        _heads(dec_o, "dec_o"), _ptr(dec_y), 0 if dec_y is None else _rows(dec_y, "dec_y"), B, int(bool(silu)),
+        _ptr(state), state.shape[0], num_k_heads, HV, dk, dv, float(scale), int(bool(qk_l2norm)),
+        _stream(stream))
+    _check(rc, "gdn_chunk_rule_and_fused_decode")

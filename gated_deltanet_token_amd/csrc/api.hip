@@ -39,7 +39,8 @@ Span row_span(const void *p, int64_t rows, int64_t stride, int64_t cols, int64_t
     if (rows <= 0 || cols <= 0) return {lo, lo};
     return {lo, lo + (uintptr_t)(((rows - 1) * stride + cols) * elem)};
 }
-bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+// empty ranges overlap nothing
+bool overlap(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
 
 int hip_status(hipError_t e, const char *what) {
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -202,20 +203,19 @@ GDN_EXPORT size_t gdn_chunk_workspace_size(int32_t num_seqs, int32_t num_tokens,
     return (size_t)gdn::chunk_workspace_bytes(num_seqs, num_tokens, num_k_heads, num_v_heads);
 }
 
-GDN_EXPORT int gdn_chunk_gated_delta_rule(const gdn_bf16 *q, int64_t q_stride, const gdn_bf16 *k, int64_t k_stride,
-                                          const gdn_bf16 *v, int64_t v_stride, const float *g, const float *beta,
-                                          float *state, int32_t num_slots, const int32_t *query_start_loc,
-                                          const int32_t *state_indices, const uint8_t *has_initial_state,
-                                          gdn_bf16 *o, int64_t o_stride, int32_t num_seqs, int32_t num_tokens,
-                                          int32_t num_k_heads, int32_t num_v_heads, int32_t head_k_dim,
-                                          int32_t head_v_dim, void *workspace, size_t workspace_bytes,
-                                          float scale, int32_t qk_l2norm, void *stream) {
+namespace {
+
+// the chunkwise call's checks; 1 = nothing to do, with GDN_OK recorded
+int check_chunk(const gdn_bf16 *q, int64_t q_stride, const gdn_bf16 *k, int64_t k_stride, const gdn_bf16 *v,
+                int64_t v_stride, const float *g, const float *beta, float *state, int32_t num_slots,
+                const int32_t *query_start_loc, const int32_t *state_indices, const uint8_t *has_initial_state,
+                gdn_bf16 *o, int64_t o_stride, int32_t num_seqs, int32_t num_tokens, int32_t num_k_heads,
+                int32_t num_v_heads, int32_t head_k_dim, int32_t head_v_dim, void *workspace,
+                size_t workspace_bytes, float scale, int32_t qk_l2norm, gdn::RecurrentArgs &a) {
     if (!query_start_loc) return fail(GDN_ERR_INVALID, "query_start_loc is required");
-    gdn::RecurrentArgs a;
     const int rc = check_recurrent(q, q_stride, k, k_stride, v, v_stride, g, beta, state, num_slots,
                                    query_start_loc, state_indices, has_initial_state, o, o_stride, num_seqs,
                                    num_tokens, num_k_heads, num_v_heads, head_k_dim, head_v_dim, scale, qk_l2norm, a);
-    if (rc == 1) return GDN_OK;
     if (rc) return rc;
     if (head_k_dim != 128) return fail(GDN_ERR_UNSUPPORTED, "chunked form: head_k_dim must be 128");
     if (head_v_dim % 32) return fail(GDN_ERR_UNSUPPORTED, "chunked form: head_v_dim must be a multiple of 32");
@@ -238,17 +238,37 @@ GDN_EXPORT int gdn_chunk_gated_delta_rule(const gdn_bf16 *q, int64_t q_stride, c
         overlap(ws, row_span(v, num_tokens, v_stride, v_w, 2)) || overlap(ws, row_span(o, num_tokens, o_stride, v_w, 2)) ||
         overlap(ws, st) || overlap(ws, gs) || overlap(ws, bs))
         return fail(GDN_ERR_INVALID, "workspace overlaps q, k, v, g, beta, state or o");
+    return GDN_OK;
+}
+
+}  // namespace
+
+GDN_EXPORT int gdn_chunk_gated_delta_rule(const gdn_bf16 *q, int64_t q_stride, const gdn_bf16 *k, int64_t k_stride,
+                                          const gdn_bf16 *v, int64_t v_stride, const float *g, const float *beta,
+                                          float *state, int32_t num_slots, const int32_t *query_start_loc,
+                                          const int32_t *state_indices, const uint8_t *has_initial_state,
+                                          gdn_bf16 *o, int64_t o_stride, int32_t num_seqs, int32_t num_tokens,
+                                          int32_t num_k_heads, int32_t num_v_heads, int32_t head_k_dim,
+                                          int32_t head_v_dim, void *workspace, size_t workspace_bytes,
+                                          float scale, int32_t qk_l2norm, void *stream) {
+    gdn::RecurrentArgs a;
+    const int rc = check_chunk(q, q_stride, k, k_stride, v, v_stride, g, beta, state, num_slots, query_start_loc,
+                               state_indices, has_initial_state, o, o_stride, num_seqs, num_tokens, num_k_heads,
+                               num_v_heads, head_k_dim, head_v_dim, workspace, workspace_bytes, scale, qk_l2norm, a);
+    if (rc == 1) return GDN_OK;
+    if (rc) return rc;
     return hip_status(gdn::launch_chunk_recurrent(a, workspace, num_tokens, (hipStream_t)stream),
                       "chunk recurrent launch");
 }
 
-GDN_EXPORT int gdn_fused_conv_decode(const gdn_bf16 *x, int64_t x_stride, const gdn_bf16 *conv_weight,
-                                     const gdn_bf16 *conv_bias, gdn_bf16 *conv_state, int32_t num_conv_slots,
-                                     const float *g, const float *beta, float *state, int32_t num_slots,
-                                     const int32_t *state_indices, gdn_bf16 *o, int64_t o_stride, gdn_bf16 *y,
-                                     int64_t y_stride, int32_t batch, int32_t num_k_heads, int32_t num_v_heads,
-                                     int32_t head_k_dim, int32_t head_v_dim, int32_t silu, float scale,
-                                     int32_t qk_l2norm, void *stream) {
+namespace {
+
+// the fused decode call's checks; 1 = nothing to do, with GDN_OK recorded
+int check_fused(const gdn_bf16 *x, int64_t x_stride, const gdn_bf16 *conv_weight, const gdn_bf16 *conv_bias,
+                gdn_bf16 *conv_state, int32_t num_conv_slots, const float *g, const float *beta, float *state,
+                int32_t num_slots, const int32_t *state_indices, gdn_bf16 *o, int64_t o_stride, gdn_bf16 *y,
+                int64_t y_stride, int32_t batch, int32_t num_k_heads, int32_t num_v_heads, int32_t head_k_dim,
+                int32_t head_v_dim, int32_t silu, float scale, int32_t qk_l2norm, gdn::FusedDecodeArgs &a) {
     if (!x || !conv_weight || !conv_state || !g || !beta || !state || !state_indices || !o)
         return fail(GDN_ERR_INVALID, "x, conv_weight, conv_state, g, beta, state, state_indices and o are required");
     if (batch < 0) return fail(GDN_ERR_INVALID, "negative batch");
@@ -287,9 +307,103 @@ GDN_EXPORT int gdn_fused_conv_decode(const gdn_bf16 *x, int64_t x_stride, const 
         if (overlap(xs, ys) || overlap(os, ys) || overlap(ys, sts) || overlap(ys, css))
             return fail(GDN_ERR_INVALID, "y overlaps x, o, state or conv_state");
     }
-    if (batch == 0) return ok();
-    gdn::FusedDecodeArgs a{x, x_stride, conv_weight, conv_bias, conv_state, (int)channels, g, beta, state,
-                           state_indices, o, o_stride, y, y_stride, batch, num_k_heads, num_v_heads, head_k_dim,
-                           head_v_dim, scale, qk_l2norm, silu};
+    if (batch == 0) {
+        ok();
+        return 1;
+    }
+    a = gdn::FusedDecodeArgs{x, x_stride, conv_weight, conv_bias, conv_state, (int)channels, g, beta, state,
+                             state_indices, o, o_stride, y, y_stride, batch, num_k_heads, num_v_heads, head_k_dim,
+                             head_v_dim, scale, qk_l2norm, silu};
+    return GDN_OK;
+}
+
+}  // namespace
+
+GDN_EXPORT int gdn_fused_conv_decode(const gdn_bf16 *x, int64_t x_stride, const gdn_bf16 *conv_weight,
+                                     const gdn_bf16 *conv_bias, gdn_bf16 *conv_state, int32_t num_conv_slots,
+                                     const float *g, const float *beta, float *state, int32_t num_slots,
+                                     const int32_t *state_indices, gdn_bf16 *o, int64_t o_stride, gdn_bf16 *y,
+                                     int64_t y_stride, int32_t batch, int32_t num_k_heads, int32_t num_v_heads,
+                                     int32_t head_k_dim, int32_t head_v_dim, int32_t silu, float scale,
+                                     int32_t qk_l2norm, void *stream) {
+    gdn::FusedDecodeArgs a;
+    const int rc = check_fused(x, x_stride, conv_weight, conv_bias, conv_state, num_conv_slots, g, beta, state,
+                               num_slots, state_indices, o, o_stride, y, y_stride, batch, num_k_heads, num_v_heads,
+                               head_k_dim, head_v_dim, silu, scale, qk_l2norm, a);
+    if (rc == 1) return GDN_OK;
+    if (rc) return rc;
     return hip_status(gdn::launch_fused_conv_decode(a, (hipStream_t)stream), "fused conv decode launch");
+}
+
+GDN_EXPORT int gdn_chunk_rule_and_fused_decode(
+    const gdn_bf16 *q, int64_t q_stride, const gdn_bf16 *k, int64_t k_stride, const gdn_bf16 *v, int64_t v_stride,
+    const float *g, const float *beta, const int32_t *query_start_loc, const int32_t *state_indices,
+    const uint8_t *has_initial_state, gdn_bf16 *o, int64_t o_stride, int32_t num_seqs, int32_t num_tokens,
+    void *workspace, size_t workspace_bytes, const gdn_bf16 *dec_x, int64_t dec_x_stride,
+    const gdn_bf16 *conv_weight, const gdn_bf16 *conv_bias, gdn_bf16 *conv_state, int32_t num_conv_slots,
+    const float *dec_g, const float *dec_beta, const int32_t *dec_state_indices, gdn_bf16 *dec_o,
+    int64_t dec_o_stride, gdn_bf16 *dec_y, int64_t dec_y_stride, int32_t dec_batch, int32_t silu, float *state,
+    int32_t num_slots, int32_t num_k_heads, int32_t num_v_heads, int32_t head_k_dim, int32_t head_v_dim,
+    float scale, int32_t qk_l2norm, void *stream) {
+    // an empty half is skipped unchecked (its pointers may be NULL)
+    gdn::RecurrentArgs a;
+    const int rc_c = num_seqs == 0 || num_tokens == 0
+                         ? (num_seqs < 0 || num_tokens < 0 ? fail(GDN_ERR_INVALID, "negative num_seqs or num_tokens")
+                                                           : 1)
+                         : check_chunk(q, q_stride, k, k_stride, v, v_stride, g, beta, state, num_slots,
+                                       query_start_loc, state_indices, has_initial_state, o, o_stride, num_seqs,
+                                       num_tokens, num_k_heads, num_v_heads, head_k_dim, head_v_dim, workspace,
+                                       workspace_bytes, scale, qk_l2norm, a);
+    if (rc_c < 0) return rc_c;
+    gdn::FusedDecodeArgs f;
+    const int rc_f = dec_batch == 0
+                         ? 1
+                         : check_fused(dec_x, dec_x_stride, conv_weight, conv_bias, conv_state, num_conv_slots,
+                                       dec_g, dec_beta, state, num_slots, dec_state_indices, dec_o, dec_o_stride,
+                                       dec_y, dec_y_stride, dec_batch, num_k_heads, num_v_heads, head_k_dim,
+                                       head_v_dim, silu, scale, qk_l2norm, f);
+    if (rc_f < 0) return rc_f;
+    ok();
+    // the two halves run at the same time: what one writes must be none of
+    // the other's operands (the shared state pool aside: its slots must be
+    // distinct across both halves, a precondition not checked here)
+    const int64_t qk_w = (int64_t)num_k_heads * head_k_dim, v_w = (int64_t)num_v_heads * head_v_dim;
+    const int64_t channels = 2 * qk_w + v_w;
+    const int64_t nt = rc_c == 1 ? 0 : num_tokens, nb = rc_f == 1 ? 0 : dec_batch;
+    const Span p_in[] = {row_span(q, nt, q_stride, qk_w, 2), row_span(k, nt, k_stride, qk_w, 2),
+                         row_span(v, nt, v_stride, v_w, 2),
+                         {(uintptr_t)g, (uintptr_t)g + (uintptr_t)(nt * num_v_heads * 4)},
+                         {(uintptr_t)beta, (uintptr_t)beta + (uintptr_t)(nt * num_v_heads * 4)}};
+    const Span p_out[] = {row_span(o, nt, o_stride, v_w, 2),
+                          {(uintptr_t)workspace,
+                           (uintptr_t)workspace + (nt ? (uintptr_t)gdn::chunk_workspace_bytes(
+                                                            num_seqs, num_tokens, num_k_heads, num_v_heads)
+                                                      : 0)}};
+    const Span d_in[] = {row_span(dec_x, nb, dec_x_stride, channels, 2),
+                         {(uintptr_t)conv_weight, (uintptr_t)conv_weight + (uintptr_t)(nb ? channels * 4 * 2 : 0)},
+                         {(uintptr_t)conv_bias,
+                          (uintptr_t)conv_bias + (uintptr_t)(nb && conv_bias ? channels * 2 : 0)},
+                         {(uintptr_t)dec_g, (uintptr_t)dec_g + (uintptr_t)(nb * num_v_heads * 4)},
+                         {(uintptr_t)dec_beta, (uintptr_t)dec_beta + (uintptr_t)(nb * num_v_heads * 4)}};
+    const Span d_out[] = {row_span(dec_o, nb, dec_o_stride, v_w, 2),
+                          row_span(dec_y, dec_y ? nb : 0, dec_y_stride, channels, 2),
+                          {(uintptr_t)conv_state,
+                           (uintptr_t)conv_state + (uintptr_t)(nb ? (int64_t)num_conv_slots * 3 * channels * 2 : 0)}};
+    for (const Span &w : p_out) {
+        for (const Span &r : d_in)
+            if (overlap(w, r)) return fail(GDN_ERR_INVALID, "a prefill output (o, workspace) overlaps a decode input");
+        for (const Span &r : d_out)
+            if (overlap(w, r)) return fail(GDN_ERR_INVALID, "a prefill output (o, workspace) overlaps a decode output");
+    }
+    for (const Span &w : d_out)
+        for (const Span &r : p_in)
+            if (overlap(w, r))
+                return fail(GDN_ERR_INVALID, "a decode output (o, y, conv_state) overlaps a prefill input");
+    if (rc_c == 1 && rc_f == 1) return GDN_OK;
+    if (rc_c == 1) return hip_status(gdn::launch_fused_conv_decode(f, (hipStream_t)stream), "fused conv decode launch");
+    if (rc_f == 1)
+        return hip_status(gdn::launch_chunk_recurrent(a, workspace, num_tokens, (hipStream_t)stream),
+                          "chunk recurrent launch");
+    return hip_status(gdn::launch_chunk_and_decode(a, workspace, num_tokens, f, (hipStream_t)stream),
+                      "chunk and decode launch");
 }

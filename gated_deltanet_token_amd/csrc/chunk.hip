@@ -29,6 +29,7 @@
 // significant bits) and sums the partial products.  T is inverted in fp32
 // (16 x 16 diagonal blocks by substitution, off-diagonal blocks with fp32
 // MFMA).
+#include "fused_unit.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -489,14 +490,18 @@ struct RowStage {
     uint4 sc;                                          // threads < 80: 4 scalars of one of 5 arrays
 };
 
-template <int NW>
-__global__ __launch_bounds__(64 * NW, 1) void chunk_scan_rows_kernel(RecurrentArgs a, const ChunkRec *recs,
-                                                                     const KtRec *kts, int n_vblocks) {
+// One scan workgroup's work: the 16 NW v rows from 16 NW vb of one
+// (sequence s, v-head h), work = (s HV + h) n_vblocks + vb, through that
+// sequence's chunks.  Called by all 64 NW threads of a workgroup; sm is the
+// workgroup's LDS.  Each kernel inlines its own instance (TAG): with one
+// instance shared by two kernels, hipcc 7.2 scheduled the scan kernel's loop
+// with 26 more AGPR moves.
+template <int NW, int TAG = 0>
+__device__ __forceinline__ void scan_rows_unit(const RecurrentArgs &a, const ChunkRec *recs, const KtRec *kts,
+                                               int n_vblocks, int work, RowScanSmem<NW> &sm) {
     using St = RowStage<NW>;
     constexpr int NT = St::NT, DVB = St::DVB;
-    __shared__ RowScanSmem<NW> sm;
     const int HV = a.num_v_heads;
-    const int work = xcd_contiguous(blockIdx.x, gridDim.x);
     const int vb = work % n_vblocks;
     const int sh = work / n_vblocks;
     const int h = sh % HV;
@@ -744,6 +749,44 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_scan_rows_kernel(RecurrentAr
     for (int dt = 0; dt < 8; ++dt) store_stream4(S_g + 16 * dt, S[dt]);
 }
 
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void chunk_scan_rows_kernel(RecurrentArgs a, const ChunkRec *recs,
+                                                                     const KtRec *kts, int n_vblocks) {
+    __shared__ RowScanSmem<NW> sm;
+    scan_rows_unit<NW>(a, recs, kts, n_vblocks, xcd_contiguous(blockIdx.x, gridDim.x), sm);
+}
+
+// The scan and a batch of fused decode units (fused_unit.h) in one grid, for
+// an engine step that holds both prefill chunks and decode rows.  Blocks
+// [0, n_scan_pad) are scan workgroups (n_scan_pad: the scan's count rounded
+// up to a multiple of the XCD count; the extra ones exit at once), the rest
+// decode units.  Workgroups are dispatched in block order, so the scan --
+// the step's long serial chain -- starts first on as many CUs as it has
+// workgroups; the decode units fill the other CUs and then each CU a scan
+// workgroup releases.  Each role runs its own kernel's code on its own
+// operands, so results are bit-identical to the two launches.  The kernel
+// has the scan's LDS and registers, so a CU holds one decode unit at a time
+// where the decode kernel fits two.
+constexpr int kMixedThreads = 256;
+static_assert(kFusedThreads == kMixedThreads, "decode units and 64-row scan workgroups are both 4 waves");
+static_assert(sizeof(RowScanSmem<4>) >= kMaxGroupChannels * sizeof(uint16_t),
+              "a decode unit's conv output fits in the scan's LDS");
+
+__global__ __launch_bounds__(kMixedThreads, 1) void chunk_scan_decode_kernel(RecurrentArgs a, const ChunkRec *recs,
+                                                                           const KtRec *kts, int n_vblocks,
+                                                                           int n_scan, int n_scan_pad,
+                                                                           FusedDecodeArgs f, int n_dec) {
+    __shared__ RowScanSmem<4> sm;
+    const int bid = blockIdx.x;
+    if (bid < n_scan_pad) {
+        if (bid < n_scan) scan_rows_unit<4, 1>(a, recs, kts, n_vblocks, xcd_contiguous(bid, n_scan), sm);
+    } else {
+        // n_scan_pad is a multiple of the XCD count: bid - n_scan_pad stays on bid's XCD
+        fused_decode_unit<DKC, kFusedRows>(f, xcd_contiguous(bid - n_scan_pad, n_dec),
+                                           reinterpret_cast<uint16_t *>(&sm));
+    }
+}
+
 }  // namespace
 
 int64_t chunk_max_chunks(int num_seqs, int num_tokens) {
@@ -755,36 +798,84 @@ int64_t chunk_workspace_bytes(int num_seqs, int num_tokens, int num_k_heads, int
     return mc * ((int64_t)num_v_heads * (int64_t)sizeof(ChunkRec) + (int64_t)num_k_heads * (int64_t)sizeof(KtRec));
 }
 
-hipError_t launch_chunk_recurrent(const RecurrentArgs &a, void *workspace, int num_tokens, hipStream_t stream) {
+namespace {
+
+struct ChunkLaunch {
+    ChunkRec *recs;
+    KtRec *kts;
+    long long prep_blocks, scan_blocks;
+    int nvb;
+    bool wide;
+};
+
+ChunkLaunch chunk_launch(const RecurrentArgs &a, void *workspace, int num_tokens) {
+    ChunkLaunch c;
     const int64_t mc = chunk_max_chunks(a.num_seqs, num_tokens);
-    ChunkRec *recs = reinterpret_cast<ChunkRec *>(workspace);
-    KtRec *kts = reinterpret_cast<KtRec *>(reinterpret_cast<char *>(workspace) +
-                                           mc * a.num_v_heads * (int64_t)sizeof(ChunkRec));
-    const long long prep_blocks = mc * a.num_v_heads;
+    c.recs = reinterpret_cast<ChunkRec *>(workspace);
+    c.kts = reinterpret_cast<KtRec *>(reinterpret_cast<char *>(workspace) +
+                                      mc * a.num_v_heads * (int64_t)sizeof(ChunkRec));
+    c.prep_blocks = mc * a.num_v_heads;
     // 64 v rows (four waves) per workgroup whenever head_v_dim allows: each
     // chunk's operands then serve twice the rows, which measured faster at
     // every prefill shape tried (one to three sequences, 500 to 2048 tokens),
     // even where 32-row workgroups would have used twice the CUs
-    const long long heads = (long long)a.num_seqs * a.num_v_heads;
-    const bool wide = (a.dv % 64) == 0;
-    const int nvb = a.dv / (wide ? 64 : 32);
-    const long long scan_blocks = heads * nvb;
-    if (scan_blocks == 0) return hipSuccess;
-    if (prep_blocks > 0x7fffffffLL || scan_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    c.wide = (a.dv % 64) == 0;
+    c.nvb = a.dv / (c.wide ? 64 : 32);
+    c.scan_blocks = (long long)a.num_seqs * a.num_v_heads * c.nvb;
+    return c;
+}
+
+hipError_t launch_prep(const RecurrentArgs &a, const ChunkLaunch &c, hipStream_t stream) {
     // two v-heads per prep workgroup whenever the v-heads of a q/k head pair up
     if ((a.num_v_heads / a.num_k_heads) % 2 == 0)
-        hipLaunchKernelGGL(chunk_prep_kernel<2>, dim3((unsigned)(prep_blocks / 2)), dim3(2 * NTH), 0, stream, a, recs,
-                           kts);
+        hipLaunchKernelGGL(chunk_prep_kernel<2>, dim3((unsigned)(c.prep_blocks / 2)), dim3(2 * NTH), 0, stream, a,
+                           c.recs, c.kts);
     else
-        hipLaunchKernelGGL(chunk_prep_kernel<1>, dim3((unsigned)prep_blocks), dim3(NTH), 0, stream, a, recs, kts);
-    hipError_t e = hipGetLastError();
+        hipLaunchKernelGGL(chunk_prep_kernel<1>, dim3((unsigned)c.prep_blocks), dim3(NTH), 0, stream, a, c.recs,
+                           c.kts);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const RecurrentArgs &a, const ChunkLaunch &c, hipStream_t stream) {
+    if (c.wide)
+        hipLaunchKernelGGL(chunk_scan_rows_kernel<4>, dim3((unsigned)c.scan_blocks), dim3(256), 0, stream, a, c.recs,
+                           c.kts, c.nvb);
+    else
+        hipLaunchKernelGGL(chunk_scan_rows_kernel<2>, dim3((unsigned)c.scan_blocks), dim3(128), 0, stream, a, c.recs,
+                           c.kts, c.nvb);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_recurrent(const RecurrentArgs &a, void *workspace, int num_tokens, hipStream_t stream) {
+    const ChunkLaunch c = chunk_launch(a, workspace, num_tokens);
+    if (c.scan_blocks == 0) return hipSuccess;
+    if (c.prep_blocks > 0x7fffffffLL || c.scan_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipError_t e = launch_prep(a, c, stream);
     if (e != hipSuccess) return e;
-    if (wide)
-        hipLaunchKernelGGL(chunk_scan_rows_kernel<4>, dim3((unsigned)scan_blocks), dim3(256), 0, stream, a, recs, kts,
-                           nvb);
-    else
-        hipLaunchKernelGGL(chunk_scan_rows_kernel<2>, dim3((unsigned)scan_blocks), dim3(128), 0, stream, a, recs, kts,
-                           nvb);
+    return launch_scan(a, c, stream);
+}
+
+hipError_t launch_chunk_and_decode(const RecurrentArgs &a, void *workspace, int num_tokens,
+                                   const FusedDecodeArgs &f, hipStream_t stream) {
+    const ChunkLaunch c = chunk_launch(a, workspace, num_tokens);
+    const long long n_dec = (long long)f.batch * f.num_k_heads;
+    if (c.scan_blocks == 0) return launch_fused_conv_decode(f, stream);
+    if (n_dec == 0) return launch_chunk_recurrent(a, workspace, num_tokens, stream);
+    const long long n_scan_pad = (c.scan_blocks + kNumXcd - 1) / kNumXcd * kNumXcd;
+    if (c.prep_blocks > 0x7fffffffLL || n_scan_pad + n_dec > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipError_t e = launch_prep(a, c, stream);
+    if (e != hipSuccess) return e;
+    // one grid where the scan runs in 64-row workgroups and the decode in
+    // 128-wide rows; other shapes take the two launches
+    if (!c.wide || f.dk != DKC) {
+        e = launch_scan(a, c, stream);
+        if (e != hipSuccess) return e;
+        return launch_fused_conv_decode(f, stream);
+    }
+    hipLaunchKernelGGL(chunk_scan_decode_kernel, dim3((unsigned)(n_scan_pad + n_dec)), dim3(kMixedThreads), 0, stream,
+                       a, c.recs, c.kts, c.nvb, (int)c.scan_blocks, (int)n_scan_pad, f, (int)n_dec);
     return hipGetLastError();
 }
 

@@ -1,0 +1,139 @@
+// One unit of the fused decode step -- (sequence, q/k head): the conv update
+// of that head group's channels and the gated delta rule on its state rows
+// -- as a device function, so that the decode kernel and the mixed-step
+// kernel (chunk scan and decode in one grid) run the same code and give
+// bit-identical results.
+//
+// One unit owns every conv channel its head group reads -- its q and k
+// channels and the v channels of the v heads that share the q/k head -- and
+// all state rows of those v heads.  So each conv_state channel has exactly
+// one reader-writer (no race between reading the old window and writing the
+// new one), and the conv output never leaves the workgroup: it is rounded
+// to bf16 (as the two-call path stores it), kept in LDS and consumed by the
+// recurrence.
+#pragma once
+
+#include "conv_math.h"
+#include "gdn_device.h"
+#include "gdn_internal.h"
+#include "gdr_math.h"
+
+namespace gdn {
+
+// 4 waves, 8 state rows per lane group: at the decode shape (2 v heads of
+// 128 rows per q/k head) one pass covers the whole group, and the 512
+// workgroups of a 32-sequence batch are all resident at once on 256 CUs.
+constexpr int kFusedThreads = 256;
+constexpr int kFusedRows = 8;                      // rows per lane group per pass
+constexpr int kMaxGroupChannels = 8192;            // q + k + v channels of one head group
+
+// bid: the unit, b * num_k_heads + hk.  act: LDS for the conv output of the
+// group, (2 DK + (HV / HK) dv) bf16.  Called by all kFusedThreads threads of
+// a workgroup.
+template <int DK, int R>
+__device__ __forceinline__ void fused_decode_unit(const FusedDecodeArgs &a, int bid, uint16_t *act) {
+    using L = RowLayout<DK>;
+    constexpr int G = L::G, E = L::E, M = L::M;
+    constexpr int ROWS_PER_PASS = kFusedThreads / G;          // rows covered once per lane
+
+    const int HK = a.num_k_heads, HV = a.num_v_heads, grp = HV / HK;
+    const int b = bid / HK;
+    const int hk = bid - b * HK;
+    const int slot = a.state_indices[b];
+    if (slot < 0) return;
+    const int tid = threadIdx.x;
+    const int dv = a.dv;
+    const int nq = DK, nv = grp * dv;                         // channels: q and k DK each, v grp*dv
+    const int n_vec = (2 * nq + nv) / kConvVec;
+    const int j = (tid & 63) % G;
+    const int n_rows = nv;
+
+    // one pass of state rows: row r of this lane group, loaded as streaming
+    // 16-byte vectors (each state element is read and written once)
+    int row[R];
+    bool valid[R];
+    float S[R][E];
+    auto load_rows = [&](int base) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            row[r] = base + r * ROWS_PER_PASS + tid / G;      // row within the group
+            valid[r] = row[r] < n_rows;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int h = hk * grp + row[r] / dv, i = row[r] % dv;
+            const float *Sp = a.state + (((int64_t)slot * HV + h) * dv + i) * DK + 4 * j;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                f32x4 v4 = {0.f, 0.f, 0.f, 0.f};
+                if (valid[r]) v4 = load_stream4(Sp + 4 * G * m);
+                S[r][4 * m + 0] = v4.x;
+                S[r][4 * m + 1] = v4.y;
+                S[r][4 * m + 2] = v4.z;
+                S[r][4 * m + 3] = v4.w;
+            }
+        }
+    };
+
+    // ---- conv update of the group's channels.  The first pass of state
+    // loads is issued right after the conv loads: it does not depend on the
+    // conv, so its latency overlaps the conv arithmetic and the barrier.
+    for (int c = tid; c < n_vec; c += kFusedThreads) {
+        const int lc = c * kConvVec;                          // channel within the group (q | k | v)
+        int ch;                                               // channel within the conv row
+        if (lc < nq) ch = hk * DK + lc;
+        else if (lc < 2 * nq) ch = HK * DK + hk * DK + (lc - nq);
+        else ch = 2 * HK * DK + hk * nv + (lc - 2 * nq);
+        uint16_t *st = a.conv_state + (int64_t)slot * 3 * a.channels + ch;
+        const uint4 s0 = *reinterpret_cast<const uint4 *>(st);
+        const uint4 s1 = *reinterpret_cast<const uint4 *>(st + a.channels);
+        const uint4 s2 = *reinterpret_cast<const uint4 *>(st + 2 * (int64_t)a.channels);
+        const uint4 xv = *reinterpret_cast<const uint4 *>(a.x + (int64_t)b * a.x_stride + ch);
+        ConvTaps taps;
+        load_taps(taps, a.conv_weight, a.conv_bias, ch);
+        if (c == tid) load_rows(0);
+        const uint4 out = conv_row(taps, s0, s1, s2, xv, a.silu != 0);
+        *reinterpret_cast<uint4 *>(st) = s1;
+        *reinterpret_cast<uint4 *>(st + a.channels) = s2;
+        *reinterpret_cast<uint4 *>(st + 2 * (int64_t)a.channels) = xv;
+        if (a.y) *reinterpret_cast<uint4 *>(a.y + (int64_t)b * a.y_stride + ch) = out;
+        *reinterpret_cast<uint4 *>(&act[lc]) = out;
+    }
+    if (tid >= n_vec) load_rows(0);
+    __syncthreads();
+
+    // ---- gated delta rule, one token, for the grp * dv rows of the group
+    float kf[E], qf[E];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qf[4 * m + e] = bf16_to_f32(act[4 * G * m + 4 * j + e]);
+            kf[4 * m + e] = bf16_to_f32(act[nq + 4 * G * m + 4 * j + e]);
+        }
+    const TokenFactors f = token_factors<G, E>(kf, qf, a.l2norm != 0);
+
+    for (int base = 0; base < n_rows; base += R * ROWS_PER_PASS) {
+        if (base > 0) load_rows(base);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int rr = min(row[r], n_rows - 1);
+            const int h = hk * grp + rr / dv, i = rr % dv;
+            const float alpha = expf(a.g[(int64_t)b * HV + h]);
+            const float beta = a.beta[(int64_t)b * HV + h];
+            const float v = bf16_to_f32(act[2 * nq + rr]);
+            const float out = row_step<G, E>(S[r], kf, qf, f, alpha, beta, v, a.scale);
+            if (valid[r]) {
+                if (j == 0) a.o[(int64_t)b * a.o_stride + (int64_t)h * dv + i] = f32_to_bf16(out);
+                float *Sp = a.state + (((int64_t)slot * HV + h) * dv + i) * DK + 4 * j;
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const f32x4 w = {S[r][4 * m + 0], S[r][4 * m + 1], S[r][4 * m + 2], S[r][4 * m + 3]};
+                    store_stream4(Sp + 4 * G * m, w);
+                }
+            }
+        }
+    }
+}
+
+}  // namespace gdn

@@ -97,5 +97,9 @@ hipError_t launch_fused_conv_decode(const FusedDecodeArgs &a, hipStream_t stream
 // chunkwise form: workspace of chunk_workspace_bytes(...) bytes, 256-byte aligned
 int64_t chunk_workspace_bytes(int num_seqs, int num_tokens, int num_k_heads, int num_v_heads);
 hipError_t launch_chunk_recurrent(const RecurrentArgs &a, void *workspace, int num_tokens, hipStream_t stream);
+// the chunkwise form and a fused decode batch on disjoint state slots, their
+// last kernels sharing one grid
+hipError_t launch_chunk_and_decode(const RecurrentArgs &a, void *workspace, int num_tokens,
+                                   const FusedDecodeArgs &f, hipStream_t stream);
 
 }  // namespace gdn

@@ -12,6 +12,10 @@
  *                               chunkwise on the matrix cores
  *   gdn_chunk_workspace_size    host: scratch bytes the chunkwise call needs
  *   gdn_fused_conv_decode       GPU: conv update + gated delta rule, one launch
+ *   gdn_chunk_rule_and_fused_decode
+ *                               GPU: the chunkwise rule on a step's prefill
+ *                               tokens and the fused decode of its decode
+ *                               rows, sharing one grid
  *
  * Conventions shared by every call
  * --------------------------------
@@ -322,6 +326,70 @@ int gdn_fused_conv_decode(const gdn_bf16 *x, int64_t x_stride,
                           int32_t batch, int32_t num_k_heads, int32_t num_v_heads,
                           int32_t head_k_dim, int32_t head_v_dim, int32_t silu,
                           float scale, int32_t qk_l2norm, void *stream);
+
+/*
+ * gdn_chunk_rule_and_fused_decode -- the recurrence of one engine step that
+ * holds both prefill tokens and decode rows (after the prefill tokens' conv):
+ * gdn_chunk_gated_delta_rule on the prefill tokens and gdn_fused_conv_decode
+ * on the decode rows, with the chunkwise form's serial scan and the decode
+ * sharing one grid.
+ *
+ * Sources: the serving workload of page "RTX 5070 Ti: close Qwen3.5-4B
+ * TTFT, TPOT, and VRAM gaps vs vLLM", section "Problem" (concurrency 32, a
+ * 2048-token batch budget), whose engine steps batch decode rows with
+ * chunked-prefill tokens; the two operations are those of the two calls
+ * named above.
+ *
+ * Why one grid: the scan walks each sequence's chunks in order on one
+ * workgroup per (sequence, v-head, 64 v rows) and leaves most CUs idle for
+ * its whole run; the decode is bandwidth-bound and independent of it.  The
+ * scan's workgroups are placed first, the decode units take the CUs left,
+ * then each CU a scan workgroup releases.
+ *
+ * Arguments:
+ *   q .. workspace_bytes  the prefill tokens, exactly as the same-named
+ *                         arguments of gdn_chunk_gated_delta_rule
+ *   dec_x .. silu         the decode rows, as the arguments x .. silu of
+ *                         gdn_fused_conv_decode (dec_g, dec_beta,
+ *                         dec_state_indices, dec_o, dec_y, dec_batch for its
+ *                         g, beta, state_indices, o, y, batch)
+ *   state .. qk_l2norm    shared by both: the layer's recurrent-state pool
+ *                         and head shape
+ * The two halves run concurrently: a state slot may be used by only one of
+ * them (state_indices and dec_state_indices disjoint, apart from negative
+ * entries; a device-side precondition, not checked).  Every result --
+ * o, dec_o, dec_y, the state slots and conv_state -- is bit-identical to
+ * calling gdn_chunk_gated_delta_rule and then gdn_fused_conv_decode (either
+ * order) with the same arguments.  An empty half (num_seqs or num_tokens 0,
+ * dec_batch 0) is skipped: its other arguments are not checked (pointers
+ * may be NULL) and overlap nothing; the call with both empty enqueues
+ * nothing.  Shapes the shared grid does not take
+ * (head_v_dim not a multiple of 64) run the two operations as consecutive
+ * launches on `stream`.
+ *
+ * Errors: every error of either call, with its arguments; GDN_ERR_INVALID
+ * when what one half writes (o, the workspace; dec_o, dec_y, conv_state)
+ * overlaps an operand of the other half (q, k, v, g, beta, o, workspace;
+ * dec_x, conv_weight, conv_bias, conv_state, dec_g, dec_beta, dec_o, dec_y).
+ */
+int gdn_chunk_rule_and_fused_decode(
+    /* prefill tokens */
+    const gdn_bf16 *q, int64_t q_stride, const gdn_bf16 *k, int64_t k_stride,
+    const gdn_bf16 *v, int64_t v_stride, const float *g, const float *beta,
+    const int32_t *query_start_loc, const int32_t *state_indices,
+    const uint8_t *has_initial_state, gdn_bf16 *o, int64_t o_stride,
+    int32_t num_seqs, int32_t num_tokens, void *workspace, size_t workspace_bytes,
+    /* decode rows */
+    const gdn_bf16 *dec_x, int64_t dec_x_stride,
+    const gdn_bf16 *conv_weight, const gdn_bf16 *conv_bias,
+    gdn_bf16 *conv_state, int32_t num_conv_slots,
+    const float *dec_g, const float *dec_beta, const int32_t *dec_state_indices,
+    gdn_bf16 *dec_o, int64_t dec_o_stride, gdn_bf16 *dec_y, int64_t dec_y_stride,
+    int32_t dec_batch, int32_t silu,
+    /* both */
+    float *state, int32_t num_slots, int32_t num_k_heads, int32_t num_v_heads,
+    int32_t head_k_dim, int32_t head_v_dim, float scale, int32_t qk_l2norm,
+    void *stream);
 
 #ifdef __cplusplus
 }

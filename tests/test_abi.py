@@ -212,3 +212,50 @@ def fused(**kw):
 ])
 def test_fused_validation(kw, code):
     assert fused(**kw) == code, gdn.lib.gdn_last_error()
+
+
+# the decode half's own g, beta, o and slots, past the workspace
+DG, DBE, DO, DIDX = (A + 0x90000000 + i * 0x1000000 for i in range(4))
+
+
+def mixed(**kw):
+    a = dict(q=Q, qs=2048, k=K_, ks=2048, v=V, vs=4096, g=G, b=BE, qsl=QSL, idx=IDX, hi=None, o=O, os=4096,
+             S=3, T=2019, ws=WS, wsb=WS_NEED,
+             x=X, xs=8192, w=W, bias=B, cs=CS, cslots=64, dg=DG, dbe=DBE, didx=DIDX, do=DO, dos=4096,
+             y=None, ys=0, B=32, silu=1,
+             st=ST, slots=64, HK=16, HV=32, dk=128, dv=128, scale=1.0, norm=1)
+    a.update(kw)
+    return gdn.lib.gdn_chunk_rule_and_fused_decode(
+        a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["g"], a["b"], a["qsl"], a["idx"], a["hi"], a["o"],
+        a["os"], a["S"], a["T"], a["ws"], a["wsb"],
+        a["x"], a["xs"], a["w"], a["bias"], a["cs"], a["cslots"], a["dg"], a["dbe"], a["didx"], a["do"], a["dos"],
+        a["y"], a["ys"], a["B"], a["silu"],
+        a["st"], a["slots"], a["HK"], a["HV"], a["dk"], a["dv"], a["scale"], a["norm"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    # each half's own checks
+    (dict(qsl=None), INV), (dict(q=None), INV), (dict(o=V), INV), (dict(wsb=WS_NEED - 1), CAP),
+    (dict(ws=WS + 128), UNS), (dict(dk=64), UNS), (dict(dv=48), UNS),
+    (dict(x=None), INV), (dict(cslots=0), INV), (dict(B=-1), INV), (dict(do=ST), INV), (dict(do=CS), INV),
+    (dict(xs=8196), UNS),
+    # what one half writes over the other half's operands
+    (dict(o=X), INV), (dict(o=W), INV), (dict(o=DG), INV), (dict(o=DBE), INV), (dict(o=DO), INV),
+    (dict(o=CS + 0x1000), INV),
+    (dict(ws=X), INV), (dict(ws=CS), INV), (dict(ws=DBE), INV), (dict(ws=DO), INV),
+    (dict(do=Q), INV), (dict(do=V + 0x100), INV), (dict(do=G), INV), (dict(do=O), INV),
+    (dict(y=BE, ys=8192), INV), (dict(y=K_, ys=8192), INV),
+    (dict(cs=V), INV), (dict(cs=Q), INV), (dict(cs=G), INV),
+])
+def test_mixed_validation(kw, code):
+    assert mixed(**kw) == code, gdn.lib.gdn_last_error()
+
+
+def test_mixed_both_halves_empty_enqueue_nothing():
+    # nothing to launch: returns GDN_OK without touching a device, and an
+    # empty half's operands overlap nothing
+    assert mixed(S=0, T=0, B=0) == gdn.GDN_OK
+    assert gdn.lib.gdn_last_error() == b""
+    assert mixed(S=0, T=0, B=0, do=Q, o=X) == gdn.GDN_OK
+    assert mixed(S=0, T=0, B=0, q=None, o=None, ws=None, x=None, do=None, st=None) == gdn.GDN_OK
+    assert mixed(S=0, T=-1, B=0) == INV and mixed(S=3, T=2019, B=-1) == INV
