@@ -2,10 +2,11 @@
 benchmark times: 128 requests x (1024 prompt + 127 decode forwards), at
 most 32 running, 2048-token chunked-prefill budget (529 engine steps,
 147,328 tokens), 8192 conv channels, 16 q/k and 32 v heads of 128, one GDN
-layer.  Per step: host-built descriptors, conv update for the decodes,
-varlen conv for the prefill chunks, the fused recurrence for the decodes and
-the chunkwise recurrence for the prefill chunks, with the conv_state and the
-recurrent state carried in 64-slot pools.
+layer.  Per step: host-built descriptors and the varlen conv for the prefill
+chunks; then the fused conv update + recurrence for a decode-only step, the
+chunkwise recurrence for a prefill-only step, and both in one call
+(gdn_chunk_rule_and_fused_decode) for a step with both; the conv_state and
+the recurrent state carried in 64-slot pools.
 
 Checks (the oracle is too slow for the whole trace; it checks sampled
 requests end to end):
@@ -59,7 +60,6 @@ def trace_run():
         y = Y[off:off + Tn]
         if nd:
             di = dev(np.array([s for (_r, _p, s) in step.decodes], np.int32))
-            gdn.gdn_causal_conv1d_update(X[off:off + nd], wt, bt, cs, di, y[:nd])
         if step.prefills:
             lens = [n for (_r, _p, n, _s, _h) in step.prefills]
             qsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
@@ -70,10 +70,15 @@ def trace_run():
         q = y[:, :HK * D].view(Tn, HK, D)
         k = y[:, HK * D:2 * HK * D].view(Tn, HK, D)
         v = y[:, 2 * HK * D:].view(Tn, HV, D)
-        if nd:
-            gdn.gdn_fused_recurrent_decode(q[:nd], k[:nd], v[:nd], G[off:off + nd], B[off:off + nd], st, di,
-                                           O[off:off + nd])
-        if step.prefills:
+        if nd and step.prefills:
+            gdn.gdn_chunk_rule_and_fused_decode(q[nd:], k[nd:], v[nd:], G[off + nd:off + Tn], B[off + nd:off + Tn],
+                                                pi, O[off + nd:off + Tn], dev(qsl), ph, X[off:off + nd], wt, bt, cs,
+                                                G[off:off + nd], B[off:off + nd], di, O[off:off + nd], st, HK,
+                                                dec_y=y[:nd], workspace=ws)
+        elif nd:
+            gdn.gdn_fused_conv_decode(X[off:off + nd], wt, bt, cs, G[off:off + nd], B[off:off + nd], st, di,
+                                      O[off:off + nd], HK, D, y=y[:nd])
+        else:
             gdn.gdn_chunk_gated_delta_rule(q[nd:], k[nd:], v[nd:], G[off + nd:off + Tn], B[off + nd:off + Tn], st, pi,
                                            O[off + nd:off + Tn], dev(qsl), ph, workspace=ws)
         for r in range(tr.n_requests):
