@@ -340,6 +340,21 @@ def cpu_baseline(seed, n_req, seq_len):
                       "rule); serial C in fp64; %.1f s" % (n_req, seq_len, elapsed)}
 
 
+def step_call_kinds(n_decodes, n_prefills, layers):
+    """The calls of one engine step in launch order: per layer, the varlen
+    conv for prefill rows, then the recurrence -- the fused decode for a
+    decode-only step, the chunkwise call for a prefill-only step, the
+    one-grid call for a step with both."""
+    per_layer = ["conv_varlen"] if n_prefills else []
+    if n_decodes and n_prefills:
+        per_layer.append("chunk_and_decode")
+    elif n_decodes:
+        per_layer.append("fused_decode")
+    elif n_prefills:
+        per_layer.append("recurrent_chunk")
+    return per_layer * layers
+
+
 def bracket_runs(kinds, kind, single_stride=1):
     """Events that bracket maximal runs of consecutive ``kind`` launches in
     ``kinds`` (the kind of every launch of a pass, as (step, call) -> kind
@@ -516,6 +531,7 @@ def main():
                                O + po * HV * D * 2, HV * D, npf, tp, HK, HV, D, D, ws.data_ptr(), ws_bytes,
                                ctypes.c_float(1.0), 1, sptr),
                               bytes_recurrent(tp, n_init, npf), flops_recurrent(tp)))
+        assert [c[0] for c in calls] == step_call_kinds(nd, npf, L)
         plans.append(calls)
 
     ch_host_ptr = ch_host.data_ptr()

@@ -82,3 +82,28 @@ def test_bracket_runs_stratified_sample(bench):
     # events come in launch order: opens and closes alternate
     flat = [e for k in sorted(br) for e in (("open", "close") if br[k] == "both" else (br[k],))]
     assert flat == ["open", "close"] * 6
+
+
+def test_plan_of_the_c32_trace(bench):
+    """The calls the bench makes over the c32 trace: one fused decode per
+    layer of a decode-only step, the conv and the one-grid call per layer of
+    a step with both kinds of rows.  The fused decode's launches then form
+    only runs of several launches (the decode-only stretches), so the
+    timed region brackets every one of them, each run with weight 1."""
+    import synth
+    tr = synth.engine_trace_schedule(0)
+    L = 4
+    kinds = [bench.step_call_kinds(len(st.decodes), len(st.prefills), L) for st in tr.steps]
+    flat = [k for ks in kinds for k in ks]
+    n_dec_only = sum(1 for st in tr.steps if st.decodes and not st.prefills)
+    n_mixed = sum(1 for st in tr.steps if st.decodes and st.prefills)
+    n_pre_only = sum(1 for st in tr.steps if st.prefills and not st.decodes)
+    assert n_dec_only + n_mixed + n_pre_only == len(tr.steps) == 529
+    assert flat.count("fused_decode") == L * n_dec_only
+    assert flat.count("chunk_and_decode") == L * n_mixed
+    assert flat.count("recurrent_chunk") == L * n_pre_only
+    assert flat.count("conv_varlen") == L * (n_mixed + n_pre_only)
+    br, n_ev, wts, n_timed = bench.bracket_runs(kinds, "fused_decode", bench.ROOFLINE_STRIDE)
+    assert n_timed == flat.count("fused_decode")
+    assert wts and all(w == 1.0 for w in wts)
+    assert n_ev == 2 * len(wts) == 8          # four decode-only stretches
