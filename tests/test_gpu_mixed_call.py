@@ -59,23 +59,24 @@ def operands(d):
                 st=dev(d["state"]))
 
 
-def run_mixed(d):
+def run_mixed(d, scale=1.0, norm=True, hi=True):
     t = operands(d)
     gdn.gdn_chunk_rule_and_fused_decode(t["q"], t["k"], t["v"], t["g"], t["beta"], t["idx"], t["o"], t["qsl"],
-                                        t["hi"], t["x"], t["w"], t["b"], t["cs"], t["dg"], t["dbeta"], t["didx"],
-                                        t["do"], t["st"], d["HK"], dec_y=t["y"])
+                                        t["hi"] if hi else None, t["x"], t["w"], t["b"], t["cs"], t["dg"],
+                                        t["dbeta"], t["didx"], t["do"], t["st"], d["HK"], dec_y=t["y"],
+                                        scale=scale, qk_l2norm=norm)
     torch.cuda.synchronize()
     return t
 
 
-def run_two_calls(d):
+def run_two_calls(d, scale=1.0, norm=True, hi=True):
     t = operands(d)
     if d["q"].shape[0]:
         gdn.gdn_chunk_gated_delta_rule(t["q"], t["k"], t["v"], t["g"], t["beta"], t["st"], t["idx"], t["o"],
-                                       t["qsl"], t["hi"])
+                                       t["qsl"], t["hi"] if hi else None, scale=scale, qk_l2norm=norm)
     if d["B"]:
         gdn.gdn_fused_conv_decode(t["x"], t["w"], t["b"], t["cs"], t["dg"], t["dbeta"], t["st"], t["didx"], t["do"],
-                                  d["HK"], DK, y=t["y"])
+                                  d["HK"], DK, y=t["y"], scale=scale, qk_l2norm=norm)
     torch.cuda.synchronize()
     return t
 
@@ -118,6 +119,25 @@ def test_mixed_call_equals_two_calls_bit_for_bit(lens, B, HK, HV, dv, slots, hi,
     used = [int(s) for s in d["state_indices"] if s >= 0] + [int(s) for s in d["didx"] if s >= 0]
     untouched = np.setdiff1d(np.arange(slots), used)
     assert np.array_equal(t1["st"].cpu().numpy()[untouched], d["state"][untouched])
+
+
+def test_mixed_call_scale_and_initial_state_reach_both_halves():
+    """scale is shared by the two halves; without has_initial_state every
+    prefill sequence starts from its slot."""
+    d = make_case(73, [129, 64], 9, 2, 4, 128, 16, [1, 1])
+    t2 = run_two_calls(d, scale=0.0884, hi=False)
+    t1 = run_mixed(d, scale=0.0884, hi=False)
+    assert_same(t1, t2)
+    HK, HV, dv, B = d["HK"], d["HV"], d["dv"], d["B"]
+    o_ref, st_ref = oracle.gated_delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"],
+                                            d["state_indices"], d["qsl"], None, 0.0884, True)
+    check_bf16(t1["o"], o_ref, "scaled prefill o")
+    y_ref, _ = oracle.causal_conv1d_update(d["x"], d["w"], d["b"], d["cs"], d["didx"])
+    yb = oracle.round_bf16(y_ref)
+    do_ref, _ = oracle.gated_delta_rule(yb[:, :HK * DK].reshape(B, HK, DK), yb[:, HK * DK:2 * HK * DK].reshape(B, HK, DK),
+                                        yb[:, 2 * HK * DK:].reshape(B, HV, dv), d["dg"], d["dbeta"], d["state"],
+                                        d["didx"], None, None, 0.0884, True)
+    check_bf16(t1["do"], do_ref, "scaled decode o")
 
 
 def test_mixed_call_against_oracle_c32_step():
