@@ -111,6 +111,11 @@ def gdn_build_conv_chunks(query_start_loc_host) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # GPU calls (torch tensors on the current HIP device)
 # ---------------------------------------------------------------------------
+# Every wrapper checks, before anything reaches the library: dtypes, the
+# shapes the head arguments imply, contiguity where the ABI assumes packed
+# data, and -- last, so that the shape checks can run without a GPU -- that
+# every tensor lives on the current GPU.  A host tensor or an undersized
+# buffer would otherwise reach the kernels as a wrong or short device range.
 
 def _torch():
     import torch
@@ -146,6 +151,87 @@ def _dtype(t, dt, name):
         raise TypeError("%s must be %s, got %s" % (name, dt, t.dtype))
 
 
+def _shape(t, shape, name):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _dims(t, n, name):
+    if t is not None and t.dim() != n:
+        raise ValueError("%s must be %d-D, got shape %s" % (name, n, tuple(t.shape)))
+
+
+def _contig(named):
+    for name, t in named:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+
+
+def _on_gpu(named):
+    """Every tensor on the current HIP device (the library's calls address
+    the current device's memory)."""
+    torch = _torch()
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError("%s must be a GPU tensor, got one on %s" % (name, t.device))
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("%s is on %s, the other operands on %s" % (name, t.device, dev))
+    if dev is not None and dev.index is not None and dev.index != torch.cuda.current_device():
+        raise ValueError("operands are on %s but the current device is cuda:%d"
+                         % (dev, torch.cuda.current_device()))
+
+
+def _workspace(workspace, need, device, stream):
+    """The caller's workspace (checked), or one allocated for this call.  An
+    allocated one is marked as used on ``stream`` so that the caching
+    allocator does not hand its memory out again before the call's kernels
+    on that stream are done with it."""
+    torch = _torch()
+    if workspace is not None:
+        _dtype(workspace, torch.uint8, "workspace")
+        _contig([("workspace", workspace)])
+        if workspace.numel() < need:
+            raise ValueError("workspace of %d bytes, %d needed" % (workspace.numel(), need))
+        return workspace
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if stream is not None:
+        ws.record_stream(stream)
+    return ws
+
+
+def _check_conv(x, weight, bias, conv_state, y, rows_name="x"):
+    torch = _torch()
+    for t, n in ((x, "x"), (weight, "weight"), (bias, "bias"), (conv_state, "conv_state"), (y, "y")):
+        _dtype(t, torch.bfloat16, n)
+    _dims(x, 2, rows_name)
+    T, C = x.shape
+    _shape(y, (T, C), "y")
+    _dims(weight, 2, "weight")
+    if weight.shape[0] != C:
+        raise ValueError("weight must have shape (%d, width), got %s" % (C, tuple(weight.shape)))
+    _shape(bias, (C,), "bias")
+    _dims(conv_state, 3, "conv_state")
+    if tuple(conv_state.shape[1:]) != (CONV_WIDTH - 1, C):
+        raise ValueError("conv_state must have shape (slots, %d, %d), got %s"
+                         % (CONV_WIDTH - 1, C, tuple(conv_state.shape)))
+    _contig([("weight", weight), ("bias", bias), ("conv_state", conv_state)])
+    return T, C
+
+
+def _check_index(t, n, name, dt):
+    _dtype(t, dt, name)
+    if t is not None:
+        _dims(t, 1, name)
+        if t.numel() != n:
+            raise ValueError("%s must have %d entries, got %d" % (name, n, t.numel()))
+        _contig([(name, t)])
+
+
 def gdn_causal_conv1d_varlen(x, weight, bias, conv_state, query_start_loc, state_indices,
                              has_initial_state, chunks, y, silu=True, stream=None):
     """Varlen causal conv (width 4) over packed tokens; see gdn.h.
@@ -153,32 +239,37 @@ def gdn_causal_conv1d_varlen(x, weight, bias, conv_state, query_start_loc, state
     x, y: bf16 [T][C] (strided rows allowed); weight bf16 [C][4]; bias bf16
     [C] or None; conv_state bf16 [slots][3][C]; query_start_loc int32 [S+1];
     state_indices int32 [S]; has_initial_state uint8 [S] or None; chunks
-    int32 [n][2] device tensor from gdn_build_conv_chunks (or None).
+    int32 [n][2] device tensor from gdn_build_conv_chunks (required when T > 0).
     """
     torch = _torch()
-    for t, n in ((x, "x"), (weight, "weight"), (bias, "bias"), (conv_state, "conv_state"), (y, "y")):
-        _dtype(t, torch.bfloat16, n)
-    _dtype(query_start_loc, torch.int32, "query_start_loc")
-    _dtype(state_indices, torch.int32, "state_indices")
-    _dtype(has_initial_state, torch.uint8, "has_initial_state")
+    T, C = _check_conv(x, weight, bias, conv_state, y)
+    _dims(state_indices, 1, "state_indices")
+    S = state_indices.numel()
+    _check_index(state_indices, S, "state_indices", torch.int32)
+    _check_index(query_start_loc, S + 1, "query_start_loc", torch.int32)
+    _check_index(has_initial_state, S, "has_initial_state", torch.uint8)
     _dtype(chunks, torch.int32, "chunks")
-    T, C = x.shape
+    if chunks is not None and (chunks.dim() != 2 or chunks.shape[1] != 2 or not chunks.is_contiguous()):
+        raise ValueError("chunks must be a contiguous int32 [n][2] tensor, got shape %s" % (tuple(chunks.shape),))
+    _on_gpu([("x", x), ("weight", weight), ("bias", bias), ("conv_state", conv_state),
+             ("query_start_loc", query_start_loc), ("state_indices", state_indices),
+             ("has_initial_state", has_initial_state), ("chunks", chunks), ("y", y)])
     n_chunks = 0 if chunks is None else chunks.shape[0]
     rc = lib.gdn_causal_conv1d_varlen(
         _ptr(x), _rows(x, "x"), _ptr(weight), _ptr(bias), _ptr(conv_state), conv_state.shape[0],
         _ptr(query_start_loc), _ptr(state_indices), _ptr(has_initial_state),
         _ptr(chunks) if n_chunks else None, n_chunks, _ptr(y), _rows(y, "y"),
-        query_start_loc.numel() - 1, T, C, weight.shape[1], int(bool(silu)), _stream(stream))
+        S, T, C, weight.shape[1], int(bool(silu)), _stream(stream))
     _check(rc, "gdn_causal_conv1d_varlen")
 
 
 def gdn_causal_conv1d_update(x, weight, bias, conv_state, state_indices, y, silu=True, stream=None):
     """Single-token conv update (decode); see gdn.h."""
     torch = _torch()
-    for t, n in ((x, "x"), (weight, "weight"), (bias, "bias"), (conv_state, "conv_state"), (y, "y")):
-        _dtype(t, torch.bfloat16, n)
-    _dtype(state_indices, torch.int32, "state_indices")
-    B, C = x.shape
+    B, C = _check_conv(x, weight, bias, conv_state, y)
+    _check_index(state_indices, B, "state_indices", torch.int32)
+    _on_gpu([("x", x), ("weight", weight), ("bias", bias), ("conv_state", conv_state),
+             ("state_indices", state_indices), ("y", y)])
     rc = lib.gdn_causal_conv1d_update(
         _ptr(x), _rows(x, "x"), _ptr(weight), _ptr(bias), _ptr(conv_state), conv_state.shape[0],
         _ptr(state_indices), _ptr(y), _rows(y, "y"), B, C, weight.shape[1], int(bool(silu)),
@@ -186,29 +277,51 @@ def gdn_causal_conv1d_update(x, weight, bias, conv_state, state_indices, y, silu
     _check(rc, "gdn_causal_conv1d_update")
 
 
-def _recurrent(func, q, k, v, g, beta, state, state_indices, o, query_start_loc, has_initial_state, scale,
-               qk_l2norm, stream, workspace=None):
+def _check_rule(q, k, v, g, beta, state, o):
+    """dtypes and shapes of a recurrence call's token tensors; returns
+    (T, HK, dk, HV, dv)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
         _dtype(t, torch.bfloat16, n)
     for t, n in ((g, "g"), (beta, "beta"), (state, "state")):
         _dtype(t, torch.float32, n)
-    _dtype(state_indices, torch.int32, "state_indices")
-    _dtype(query_start_loc, torch.int32, "query_start_loc")
-    _dtype(has_initial_state, torch.uint8, "has_initial_state")
-    if not (g.is_contiguous() and beta.is_contiguous() and state.is_contiguous()):
-        raise ValueError("g, beta and state must be contiguous")
+    _dims(q, 3, "q")
+    _dims(v, 3, "v")
     T, HK, dk = q.shape
     HV, dv = v.shape[1], v.shape[2]
+    _shape(k, (T, HK, dk), "k")
+    _shape(v, (T, HV, dv), "v")
+    _shape(o, (T, HV, dv), "o")
+    _shape(g, (T, HV), "g")
+    _shape(beta, (T, HV), "beta")
+    _dims(state, 4, "state")
+    if tuple(state.shape[1:]) != (HV, dv, dk):
+        raise ValueError("state must have shape (slots, %d, %d, %d), got %s" % (HV, dv, dk, tuple(state.shape)))
+    _contig([("g", g), ("beta", beta), ("state", state)])
+    return T, HK, dk, HV, dv
+
+
+def _recurrent(func, q, k, v, g, beta, state, state_indices, o, query_start_loc, has_initial_state, scale,
+               qk_l2norm, stream, workspace=None):
+    torch = _torch()
+    T, HK, dk, HV, dv = _check_rule(q, k, v, g, beta, state, o)
+    _dims(state_indices, 1, "state_indices")
     S = state_indices.numel()
+    _check_index(state_indices, S, "state_indices", torch.int32)
+    _check_index(query_start_loc, S + 1, "query_start_loc", torch.int32)
+    _check_index(has_initial_state, S, "has_initial_state", torch.uint8)
+    if query_start_loc is None and S != T:
+        raise ValueError("without query_start_loc there is one token per sequence: %d tokens, %d sequences"
+                         % (T, S))
+    _on_gpu([("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state", state),
+             ("state_indices", state_indices), ("o", o), ("query_start_loc", query_start_loc),
+             ("has_initial_state", has_initial_state), ("workspace", workspace)])
     args = [_ptr(q), _heads(q, "q"), _ptr(k), _heads(k, "k"), _ptr(v), _heads(v, "v"), _ptr(g),
             _ptr(beta), _ptr(state), state.shape[0], _ptr(query_start_loc), _ptr(state_indices),
             _ptr(has_initial_state), _ptr(o), _heads(o, "o"), S, T, HK, HV, dk, dv]
     if func == "gdn_chunk_gated_delta_rule":
-        need = gdn_chunk_workspace_size(S, T, HK, HV)
-        if workspace is None:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-        args += [_ptr(workspace), workspace.numel() * workspace.element_size()]
+        workspace = _workspace(workspace, gdn_chunk_workspace_size(S, T, HK, HV), q.device, stream)
+        args += [_ptr(workspace), workspace.numel()]
     args += [float(scale), int(bool(qk_l2norm)), _stream(stream)]
     _check(getattr(lib, func)(*args), func)
 
@@ -236,34 +349,97 @@ def gdn_chunk_gated_delta_rule(q, k, v, g, beta, state, state_indices, o, query_
                                workspace=None):
     """The same rule over packed prefill tokens, chunkwise on the matrix
     cores (dk = 128, dv a multiple of 32); see gdn.h.  ``workspace`` is a
-    device byte tensor of at least gdn_chunk_workspace_size(...) bytes; when
-    omitted, torch allocates one for the call."""
+    contiguous uint8 device tensor of at least gdn_chunk_workspace_size(...)
+    bytes; when omitted, torch allocates one for the call."""
+    if query_start_loc is None:
+        raise ValueError("the chunkwise call needs query_start_loc")
     _recurrent("gdn_chunk_gated_delta_rule", q, k, v, g, beta, state, state_indices, o, query_start_loc,
                has_initial_state, scale, qk_l2norm, stream, workspace)
+
+
+def _check_fused(x, conv_weight, conv_bias, conv_state, g, beta, state, state_indices, o, num_k_heads,
+                 head_k_dim, y, prefix=""):
+    """dtypes and shapes of the fused decode's operands; returns (B, HV, dv)."""
+    torch = _torch()
+    for t, n in ((x, "x"), (conv_weight, "conv_weight"), (conv_bias, "conv_bias"),
+                 (conv_state, "conv_state"), (o, "o"), (y, "y")):
+        _dtype(t, torch.bfloat16, prefix + n if n in ("x", "o", "y") else n)
+    for t, n in ((g, "g"), (beta, "beta"), (state, "state")):
+        _dtype(t, torch.float32, prefix + n if n != "state" else n)
+    _dims(o, 3, prefix + "o")
+    _dims(x, 2, prefix + "x")
+    B, HV, dv = o.shape
+    HK, dk = int(num_k_heads), int(head_k_dim)
+    C = 2 * HK * dk + HV * dv
+    _shape(x, (B, C), prefix + "x")
+    _shape(y, (B, C), prefix + "y")
+    _shape(conv_weight, (C, CONV_WIDTH), "conv_weight")
+    _shape(conv_bias, (C,), "conv_bias")
+    _dims(conv_state, 3, "conv_state")
+    if tuple(conv_state.shape[1:]) != (CONV_WIDTH - 1, C):
+        raise ValueError("conv_state must have shape (slots, %d, %d), got %s"
+                         % (CONV_WIDTH - 1, C, tuple(conv_state.shape)))
+    _shape(g, (B, HV), prefix + "g")
+    _shape(beta, (B, HV), prefix + "beta")
+    _dims(state, 4, "state")
+    if tuple(state.shape[1:]) != (HV, dv, dk):
+        raise ValueError("state must have shape (slots, %d, %d, %d), got %s" % (HV, dv, dk, tuple(state.shape)))
+    _check_index(state_indices, B, prefix + "state_indices", torch.int32)
+    _contig([("conv_weight", conv_weight), ("conv_bias", conv_bias), ("conv_state", conv_state),
+             (prefix + "g", g), (prefix + "beta", beta), ("state", state)])
+    return B, HV, dv
 
 
 def gdn_fused_conv_decode(x, conv_weight, conv_bias, conv_state, g, beta, state, state_indices, o,
                           num_k_heads, head_k_dim, y=None, silu=True, scale=1.0, qk_l2norm=True,
                           stream=None):
     """Decode step: conv update of x (q | k | v channels) fused with the gated
-    delta rule on its output; see gdn.h.  o: bf16 [B][HV][dv]; y optional."""
-    torch = _torch()
-    for t, n in ((x, "x"), (conv_weight, "conv_weight"), (conv_bias, "conv_bias"),
-                 (conv_state, "conv_state"), (o, "o"), (y, "y")):
-        _dtype(t, torch.bfloat16, n)
-    for t, n in ((g, "g"), (beta, "beta"), (state, "state")):
-        _dtype(t, torch.float32, n)
-    _dtype(state_indices, torch.int32, "state_indices")
-    if not (g.is_contiguous() and beta.is_contiguous() and state.is_contiguous()):
-        raise ValueError("g, beta and state must be contiguous")
-    B = x.shape[0]
-    HV, dv = o.shape[1], o.shape[2]
+    delta rule on its output; see gdn.h.  x: bf16 [B][2 HK dk + HV dv];
+    o: bf16 [B][HV][dv]; y optional, shaped like x."""
+    B, HV, dv = _check_fused(x, conv_weight, conv_bias, conv_state, g, beta, state, state_indices, o,
+                             num_k_heads, head_k_dim, y)
+    _on_gpu([("x", x), ("conv_weight", conv_weight), ("conv_bias", conv_bias), ("conv_state", conv_state),
+             ("g", g), ("beta", beta), ("state", state), ("state_indices", state_indices), ("o", o), ("y", y)])
     rc = lib.gdn_fused_conv_decode(
         _ptr(x), _rows(x, "x"), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state), conv_state.shape[0],
         _ptr(g), _ptr(beta), _ptr(state), state.shape[0], _ptr(state_indices), _ptr(o), _heads(o, "o"),
         _ptr(y), 0 if y is None else _rows(y, "y"), B, num_k_heads, HV, head_k_dim, dv, int(bool(silu)),
         float(scale), int(bool(qk_l2norm)), _stream(stream))
     _check(rc, "gdn_fused_conv_decode")
+
+
+def _mixed_operands(q, k, v, g, beta, state_indices, o, query_start_loc, has_initial_state, dec_x, conv_weight,
+                    conv_bias, conv_state, dec_g, dec_beta, dec_state_indices, dec_o, state, num_k_heads, dec_y):
+    """Checks of gdn_chunk_rule_and_fused_decode's operands; returns
+    (T, S, B, HK, dk, HV, dv)."""
+    torch = _torch()
+    T, HK, dk, HV, dv = _check_rule(q, k, v, g, beta, state, o)
+    if HK != int(num_k_heads):
+        raise ValueError("q has %d heads, num_k_heads is %d" % (HK, num_k_heads))
+    _dims(state_indices, 1, "state_indices")
+    S = state_indices.numel()
+    _check_index(state_indices, S, "state_indices", torch.int32)
+    _check_index(query_start_loc, S + 1, "query_start_loc", torch.int32)
+    _check_index(has_initial_state, S, "has_initial_state", torch.uint8)
+    B, HVd, dvd = _check_fused(dec_x, conv_weight, conv_bias, conv_state, dec_g, dec_beta, state, dec_state_indices,
+                               dec_o, num_k_heads, dk, dec_y, prefix="dec_")
+    if (HVd, dvd) != (HV, dv):
+        raise ValueError("dec_o has %d heads of %d, v has %d of %d" % (HVd, dvd, HV, dv))
+    return T, S, B, HK, dk, HV, dv
+
+
+def _mixed_args(q, k, v, g, beta, state_indices, o, query_start_loc, has_initial_state, dec_x, conv_weight,
+                conv_bias, conv_state, dec_g, dec_beta, dec_state_indices, dec_o, state, num_k_heads, dec_y, silu,
+                S, T, B, HV, dk, dv):
+    """The ABI arguments of the one-grid mixed call before the workspace,
+    and those after it up to (not including) the stream."""
+    pre = [_ptr(q), _heads(q, "q"), _ptr(k), _heads(k, "k"), _ptr(v), _heads(v, "v"), _ptr(g), _ptr(beta),
+           _ptr(query_start_loc), _ptr(state_indices), _ptr(has_initial_state), _ptr(o), _heads(o, "o"), S, T]
+    post = [_ptr(dec_x), _rows(dec_x, "dec_x"), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state),
+            conv_state.shape[0], _ptr(dec_g), _ptr(dec_beta), _ptr(dec_state_indices), _ptr(dec_o),
+            _heads(dec_o, "dec_o"), _ptr(dec_y), 0 if dec_y is None else _rows(dec_y, "dec_y"), B, int(bool(silu)),
+            _ptr(state), state.shape[0], num_k_heads, HV, dk, dv]
+    return pre, post
 
 
 def gdn_chunk_rule_and_fused_decode(q, k, v, g, beta, state_indices, o, query_start_loc, has_initial_state,
@@ -275,32 +451,18 @@ def gdn_chunk_rule_and_fused_decode(q, k, v, g, beta, state_indices, o, query_st
     gdn_chunk_gated_delta_rule) and the fused conv update + rule on the
     decode rows (dec_*; as gdn_fused_conv_decode), sharing the state pool
     ``state`` on distinct slots; see gdn.h."""
-    torch = _torch()
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dec_x, "dec_x"), (conv_weight, "conv_weight"),
-                 (conv_bias, "conv_bias"), (conv_state, "conv_state"), (dec_o, "dec_o"), (dec_y, "dec_y")):
-        _dtype(t, torch.bfloat16, n)
-    for t, n in ((g, "g"), (beta, "beta"), (dec_g, "dec_g"), (dec_beta, "dec_beta"), (state, "state")):
-        _dtype(t, torch.float32, n)
-    for t, n in ((state_indices, "state_indices"), (query_start_loc, "query_start_loc"),
-                 (dec_state_indices, "dec_state_indices")):
-        _dtype(t, torch.int32, n)
-    _dtype(has_initial_state, torch.uint8, "has_initial_state")
-    if not all(t.is_contiguous() for t in (g, beta, dec_g, dec_beta, state)):
-        raise ValueError("g, beta, dec_g, dec_beta and state must be contiguous")
-    T, HK, dk = q.shape
-    HV, dv = v.shape[1], v.shape[2]
-    S = state_indices.numel()
-    B = dec_x.shape[0]
-    need = gdn_chunk_workspace_size(S, T, HK, HV)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    rc = lib.gdn_chunk_rule_and_fused_decode(
-        _ptr(q), _heads(q, "q"), _ptr(k), _heads(k, "k"), _ptr(v), _heads(v, "v"), _ptr(g), _ptr(beta),
-        _ptr(query_start_loc), _ptr(state_indices), _ptr(has_initial_state), _ptr(o), _heads(o, "o"), S, T,
-        _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _ptr(dec_x), _rows(dec_x, "dec_x"), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state),
-        conv_state.shape[0], _ptr(dec_g), _ptr(dec_beta), _ptr(dec_state_indices), _ptr(dec_o),
-        _heads(dec_o, "dec_o"), _ptr(dec_y), 0 if dec_y is None else _rows(dec_y, "dec_y"), B, int(bool(silu)),
-        _ptr(state), state.shape[0], num_k_heads, HV, dk, dv, float(scale), int(bool(qk_l2norm)),
-        _stream(stream))
+    named = [("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state_indices", state_indices), ("o", o),
+             ("query_start_loc", query_start_loc), ("has_initial_state", has_initial_state), ("dec_x", dec_x),
+             ("conv_weight", conv_weight), ("conv_bias", conv_bias), ("conv_state", conv_state), ("dec_g", dec_g),
+             ("dec_beta", dec_beta), ("dec_state_indices", dec_state_indices), ("dec_o", dec_o), ("state", state),
+             ("dec_y", dec_y), ("workspace", workspace)]
+    T, S, B, HK, dk, HV, dv = _mixed_operands(*[t for _n, t in named[:18]], num_k_heads, dec_y)
+    _on_gpu(named)
+    workspace = _workspace(workspace, gdn_chunk_workspace_size(S, T, HK, HV), q.device, stream)
+    pre, post = _mixed_args(q, k, v, g, beta, state_indices, o, query_start_loc, has_initial_state, dec_x,
+                            conv_weight, conv_bias, conv_state, dec_g, dec_beta, dec_state_indices, dec_o, state,
+                            num_k_heads, dec_y, silu, S, T, B, HV, dk, dv)
+    rc = lib.gdn_chunk_rule_and_fused_decode(*pre, _ptr(workspace), workspace.numel(), *post,
+                                             float(scale), int(bool(qk_l2norm)), _stream(stream))
     _check(rc, "gdn_chunk_rule_and_fused_decode")
+

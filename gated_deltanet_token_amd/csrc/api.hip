@@ -107,13 +107,26 @@ GDN_EXPORT int gdn_causal_conv1d_varlen(const gdn_bf16 *x, int64_t x_stride, con
     if (num_seqs < 0 || n_chunks < 0) return fail(GDN_ERR_INVALID, "negative num_seqs or n_chunks");
     if ((chunks == nullptr) != (n_chunks == 0))
         return fail(GDN_ERR_INVALID, "chunks and n_chunks must be given together");
-    if (n_chunks == 0) return ok();
+    // the descriptors are the only dispatch: a call with tokens needs them
+    if (n_chunks == 0) {
+        if (num_tokens > 0)
+            return fail(GDN_ERR_INVALID, "%d tokens but no chunk descriptors (build them with gdn_build_conv_chunks)",
+                        num_tokens);
+        return ok();
+    }
     if (!query_start_loc || !state_indices) return fail(GDN_ERR_INVALID, "query_start_loc and state_indices are required");
     if (num_seqs == 0 || num_tokens == 0) return fail(GDN_ERR_INVALID, "descriptors given for an empty batch");
     if ((int64_t)n_chunks > (int64_t)num_tokens)
         return fail(GDN_ERR_INVALID, "more descriptors (%d) than tokens (%d)", n_chunks, num_tokens);
+    // each descriptor covers at most 8 tokens, so fewer than ceil(T / 8) of
+    // them cannot cover the call's tokens
+    const int64_t min_chunks = ((int64_t)num_tokens + GDN_CONV_CHUNK_TOKENS - 1) / GDN_CONV_CHUNK_TOKENS;
+    if ((int64_t)n_chunks < min_chunks)
+        return fail(GDN_ERR_INVALID, "%d descriptors cannot cover %d tokens (at least %lld needed)", n_chunks,
+                    num_tokens, (long long)min_chunks);
     gdn::ConvVarlenArgs a{x, x_stride, weight, bias, conv_state, query_start_loc, state_indices,
-                          has_initial_state, chunks, n_chunks, y, y_stride, channels, silu};
+                          has_initial_state, chunks, n_chunks, y, y_stride, channels, silu,
+                          num_seqs, num_slots, num_tokens};
     return hip_status(gdn::launch_conv_varlen(a, (hipStream_t)stream), "conv varlen launch");
 }
 
@@ -127,7 +140,8 @@ GDN_EXPORT int gdn_causal_conv1d_update(const gdn_bf16 *x, int64_t x_stride, con
     if (rc) return rc;
     if (batch == 0) return ok();
     if (!state_indices) return fail(GDN_ERR_INVALID, "state_indices is required");
-    gdn::ConvUpdateArgs a{x, x_stride, weight, bias, conv_state, state_indices, y, y_stride, batch, channels, silu};
+    gdn::ConvUpdateArgs a{x, x_stride, weight, bias, conv_state, state_indices, y, y_stride, batch, channels, silu,
+                          num_slots};
     return hip_status(gdn::launch_conv_update(a, (hipStream_t)stream), "conv update launch");
 }
 
@@ -175,7 +189,7 @@ int check_recurrent(const gdn_bf16 *q, int64_t q_stride, const gdn_bf16 *k, int6
     }
     a = gdn::RecurrentArgs{q, q_stride, k, k_stride, v, v_stride, g, beta, state, query_start_loc, state_indices,
                            has_initial_state, o, o_stride, num_seqs, num_k_heads, num_v_heads, head_k_dim,
-                           head_v_dim, scale, qk_l2norm};
+                           head_v_dim, scale, qk_l2norm, num_slots, num_tokens};
     return GDN_OK;
 }
 
@@ -313,7 +327,7 @@ int check_fused(const gdn_bf16 *x, int64_t x_stride, const gdn_bf16 *conv_weight
     }
     a = gdn::FusedDecodeArgs{x, x_stride, conv_weight, conv_bias, conv_state, (int)channels, g, beta, state,
                              state_indices, o, o_stride, y, y_stride, batch, num_k_heads, num_v_heads, head_k_dim,
-                             head_v_dim, scale, qk_l2norm, silu};
+                             head_v_dim, scale, qk_l2norm, silu, num_slots, num_conv_slots};
     return GDN_OK;
 }
 
@@ -407,3 +421,4 @@ GDN_EXPORT int gdn_chunk_rule_and_fused_decode(
     return hip_status(gdn::launch_chunk_and_decode(a, workspace, num_tokens, f, (hipStream_t)stream),
                       "chunk and decode launch");
 }
+

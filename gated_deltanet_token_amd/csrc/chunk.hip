@@ -141,8 +141,11 @@ __device__ __forceinline__ void put16(Blk &Z, const f32x4 &c, float sgn, int lan
 // the sequence s holding packed chunk `gch`, the chunk's index j in it and
 // the sequence's token range [lo, hi) (s = -1 past the last chunk); called
 // by every lane of the wave
-__device__ __forceinline__ void locate_chunk(const int32_t *qsl, int num_seqs, int gch, int &s_out, int &j_out,
-                                             int &lo_out, int &hi_out) {
+// (sequence bounds are clamped to [0, num_tokens) as everywhere in the
+// library: a malformed query_start_loc gives wrong results, never an access
+// outside the token rows or the workspace)
+__device__ __forceinline__ void locate_chunk(const int32_t *qsl, int num_seqs, int num_tokens, int gch, int &s_out,
+                                             int &j_out, int &lo_out, int &hi_out) {
     const int lane = threadIdx.x & 63;
     int before = 0;
     s_out = -1;
@@ -150,7 +153,8 @@ __device__ __forceinline__ void locate_chunk(const int32_t *qsl, int num_seqs, i
     lo_out = hi_out = 0;
     for (int s0 = 0; s0 < num_seqs; s0 += 64) {
         const int q = s0 + lane;
-        const int lo = qsl[min(q, num_seqs)], hi = qsl[min(q + 1, num_seqs)];
+        int lo, hi;
+        clamp_range(qsl[min(q, num_seqs)], qsl[min(q + 1, num_seqs)], num_tokens, lo, hi);
         int incl = q < num_seqs ? chunk_count(hi - lo) : 0;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -173,12 +177,13 @@ __device__ __forceinline__ void locate_chunk(const int32_t *qsl, int num_seqs, i
 }
 
 // number of chunks of the sequences before s; called by every lane of the wave
-__device__ __forceinline__ int chunks_before(const int32_t *qsl, int s) {
+__device__ __forceinline__ int chunks_before(const int32_t *qsl, int s, int num_tokens) {
     const int lane = threadIdx.x & 63;
     int total = 0;
     for (int s0 = 0; s0 < s; s0 += 64) {
         const int q = s0 + lane;
-        const int lo = qsl[min(q, s)], hi = qsl[min(q + 1, s)];
+        int lo, hi;
+        clamp_range(qsl[min(q, s)], qsl[min(q + 1, s)], num_tokens, lo, hi);
         int nc = q < s ? chunk_count(hi - lo) : 0;
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) nc += __shfl_xor(nc, off, 64);
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
     const int h0 = (work % NP) * VPW;           // the workgroup's first v-head
     const int gch = work / NP;                  // global chunk index
     int s, j, lo, hi;                           // (sequence, chunk within it, its tokens)
-    locate_chunk(a.qsl, a.num_seqs, gch, s, j, lo, hi);
+    locate_chunk(a.qsl, a.num_seqs, a.num_tokens, gch, s, j, lo, hi);
     // (a padded sequence, state index < 0, is prepared too: its records are
     // never read, and the row loads need not wait for the index)
     if (s < 0) return;
@@ -507,12 +512,15 @@ __device__ __forceinline__ void scan_rows_unit(const RecurrentArgs &a, const Chu
     const int h = sh % HV;
     const int s = sh / HV;
     const int slot = a.state_indices[s];
-    if (slot < 0) return;
-    const int t_begin = a.qsl[s];
-    const int t_end = a.qsl[s + 1];
+    if ((unsigned)slot >= (unsigned)a.num_slots) return;   // padding, or outside the pool
+    int t_begin, t_end;
+    clamp_range(a.qsl[s], a.qsl[s + 1], a.num_tokens, t_begin, t_end);
     if (t_end <= t_begin) return;
     const int hk = h / (HV / a.num_k_heads);
-    const int gch0 = chunks_before(a.qsl, s);
+    const int gch0 = chunks_before(a.qsl, s, a.num_tokens);
+    // the records of the sequence's chunks lie within the workspace (always,
+    // for a well-formed query_start_loc)
+    if (gch0 + chunk_count(t_end - t_begin) > (a.num_tokens + CT - 1) / CT + a.num_seqs) return;
 
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, g = lane >> 4;

@@ -29,7 +29,8 @@ __global__ __launch_bounds__(THREADS) void conv_varlen_kernel(
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ conv_state,
     const int32_t *__restrict__ qsl, const int32_t *__restrict__ state_indices,
     const uint8_t *__restrict__ has_init, const gdn_conv_chunk *__restrict__ chunks,
-    uint16_t *__restrict__ y, int64_t y_stride, int channels, int n_tiles) {
+    uint16_t *__restrict__ y, int64_t y_stride, int channels, int n_tiles, int num_seqs, int num_slots,
+    int num_tokens) {
     constexpr int TILE = THREADS * kConvVec;
     // Chunk-major and XCD-contiguous: each XCD takes one contiguous range of
     // (descriptor, channel tile) items, so a chunk's halo rows are rows its
@@ -45,13 +46,17 @@ __global__ __launch_bounds__(THREADS) void conv_varlen_kernel(
     ConvTaps taps;
     load_taps(taps, weight, bias, c0);
 
+    // A descriptor naming no sequence of the call, and a slot index outside
+    // the pool, are skipped like padding: nothing is read or written for them.
     const gdn_conv_chunk d = chunks[ci];
-    const int slot = state_indices[d.seq];
-    if (slot < 0) return;
-    const int a = qsl[d.seq];
-    const int end = qsl[d.seq + 1];
+    const bool bad = (unsigned)d.seq >= (unsigned)num_seqs || d.chunk < 0;
+    const int seq = bad ? 0 : d.seq;
+    const int slot = state_indices[seq];
+    if (bad || (unsigned)slot >= (unsigned)num_slots) return;
+    int a, end;
+    clamp_range(qsl[seq], qsl[seq + 1], num_tokens, a, end);
+    if (d.chunk >= (end - a + kChunk - 1) / kChunk) return;
     const int t0 = a + d.chunk * kChunk;
-    if (t0 >= end) return;
     const int n = min(kChunk, end - t0);
 
     uint16_t *st = conv_state + (int64_t)slot * 3 * channels + c0;
@@ -76,7 +81,7 @@ __global__ __launch_bounds__(THREADS) void conv_varlen_kernel(
         r[i] = i < kChunk - 3 ? load_stream16(p) : *reinterpret_cast<const uint4 *>(p);
     }
     // (the flag is read unconditionally, from a valid byte, for the same reason as the bias)
-    const uint8_t flag = *(has_init != nullptr ? has_init + d.seq : reinterpret_cast<const uint8_t *>(chunks + ci));
+    const uint8_t flag = *(has_init != nullptr ? has_init + seq : reinterpret_cast<const uint8_t *>(chunks + ci));
     const uint32_t keep = (first && has_init != nullptr && flag == 0) ? 0u : ~0u;
 #pragma unroll
     for (int i = 0; i < 3; ++i) h[i] = make_uint4(h[i].x & keep, h[i].y & keep, h[i].z & keep, h[i].w & keep);
@@ -119,11 +124,11 @@ __global__ __launch_bounds__(kConvThreads) void conv_update_kernel(
     const uint16_t *__restrict__ x, int64_t x_stride, const uint16_t *__restrict__ weight,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ conv_state,
     const int32_t *__restrict__ state_indices, uint16_t *__restrict__ y, int64_t y_stride,
-    int channels, int n_tiles, int silu) {
+    int channels, int n_tiles, int silu, int num_slots) {
     const int b = blockIdx.x / n_tiles;
     const int tile = blockIdx.x - b * n_tiles;
     const int slot = state_indices[b];
-    if (slot < 0) return;
+    if ((unsigned)slot >= (unsigned)num_slots) return;     // padding, or outside the pool
     const int c0 = tile * kConvTile + threadIdx.x * kConvVec;
     if (c0 >= channels) return;
     uint16_t *st = conv_state + (int64_t)slot * 3 * channels + c0;
@@ -149,11 +154,13 @@ hipError_t launch_conv_varlen_t(const ConvVarlenArgs &a, hipStream_t stream) {
     if (a.silu)
         hipLaunchKernelGGL((conv_varlen_kernel<THREADS, true>), dim3((unsigned)blocks), dim3(THREADS), 0, stream,
                            a.x, a.x_stride, a.weight, a.bias, a.conv_state, a.qsl, a.state_indices, a.has_init,
-                           a.chunks, a.y, a.y_stride, a.channels, n_tiles);
+                           a.chunks, a.y, a.y_stride, a.channels, n_tiles, a.num_seqs, a.num_slots,
+                           a.num_tokens);
     else
         hipLaunchKernelGGL((conv_varlen_kernel<THREADS, false>), dim3((unsigned)blocks), dim3(THREADS), 0, stream,
                            a.x, a.x_stride, a.weight, a.bias, a.conv_state, a.qsl, a.state_indices, a.has_init,
-                           a.chunks, a.y, a.y_stride, a.channels, n_tiles);
+                           a.chunks, a.y, a.y_stride, a.channels, n_tiles, a.num_seqs, a.num_slots,
+                           a.num_tokens);
     return hipGetLastError();
 }
 
@@ -168,7 +175,7 @@ hipError_t launch_conv_update(const ConvUpdateArgs &a, hipStream_t stream) {
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(conv_update_kernel, dim3((unsigned)blocks), dim3(kConvThreads), 0, stream,
                        a.x, a.x_stride, a.weight, a.bias, a.conv_state, a.state_indices, a.y,
-                       a.y_stride, a.channels, n_tiles, a.silu);
+                       a.y_stride, a.channels, n_tiles, a.silu, a.num_slots);
     return hipGetLastError();
 }
 

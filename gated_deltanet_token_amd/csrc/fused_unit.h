@@ -40,7 +40,8 @@ __device__ __forceinline__ void fused_decode_unit(const FusedDecodeArgs &a, int 
     const int b = bid / HK;
     const int hk = bid - b * HK;
     const int slot = a.state_indices[b];
-    if (slot < 0) return;
+    // padding, or outside either pool (the row uses the same index in both)
+    if ((unsigned)slot >= (unsigned)min(a.num_slots, a.num_conv_slots)) return;
     const int tid = threadIdx.x;
     const int dv = a.dv;
     const int nq = DK, nv = grp * dv;                         // channels: q and k DK each, v grp*dv

@@ -94,6 +94,16 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 // ---------------------------------------------------------------------------
+// A sequence's token range from query_start_loc, clamped to [0, num_tokens)
+// with hi >= lo.  For a well-formed query_start_loc this is the identity; a
+// malformed one gives wrong results but no access outside the token rows.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void clamp_range(int lo_raw, int hi_raw, int num_tokens, int &lo, int &hi) {
+    lo = min(max(lo_raw, 0), num_tokens);
+    hi = min(max(hi_raw, lo), num_tokens);
+}
+
+// ---------------------------------------------------------------------------
 // XCD-aware block order.  The dispatcher hands consecutive workgroup ids to
 // the 8 XCDs in turn; this maps them so that each XCD receives one
 // contiguous range of work items (neighbouring items share its L2).  A

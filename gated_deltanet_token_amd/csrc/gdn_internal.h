@@ -24,6 +24,9 @@ struct ConvVarlenArgs {
     int64_t y_stride;
     int channels;
     int silu;
+    int num_seqs;                // descriptors naming another sequence are skipped
+    int num_slots;               // state indices at or past it are skipped
+    int num_tokens;              // sequence ends are clamped to it
 };
 
 struct ConvUpdateArgs {
@@ -38,6 +41,7 @@ struct ConvUpdateArgs {
     int batch;
     int channels;
     int silu;
+    int num_slots;               // state indices at or past it are skipped
 };
 
 struct RecurrentArgs {
@@ -62,6 +66,8 @@ struct RecurrentArgs {
     int dv;
     float scale;
     int l2norm;
+    int num_slots;               // state indices at or past it are skipped
+    int num_tokens;              // token ranges are clamped to [0, num_tokens)
 };
 
 struct FusedDecodeArgs {
@@ -87,6 +93,8 @@ struct FusedDecodeArgs {
     float scale;
     int l2norm;
     int silu;
+    int num_slots;               // recurrent-state slots; indices at or past it are skipped
+    int num_conv_slots;          // conv_state slots; likewise
 };
 
 hipError_t launch_conv_varlen(const ConvVarlenArgs &a, hipStream_t stream);

@@ -61,9 +61,9 @@ __global__ __launch_bounds__(64 * W) void recurrent_kernel(RecurrentArgs a, int 
     const int h = sh % a.num_v_heads;
     const int s = sh / a.num_v_heads;
     const int slot = a.state_indices[s];
-    if (slot < 0) return;
-    const int t_begin = a.qsl ? a.qsl[s] : s;
-    const int t_end = a.qsl ? a.qsl[s + 1] : s + 1;
+    if ((unsigned)slot >= (unsigned)a.num_slots) return;   // padding, or outside the pool
+    int t_begin = s, t_end = s + 1;
+    if (a.qsl) clamp_range(a.qsl[s], a.qsl[s + 1], a.num_tokens, t_begin, t_end);
     if (t_end <= t_begin) return;
     const int HV = a.num_v_heads;
     const int hk = h / (HV / a.num_k_heads);
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kGroupThreads) void recurrent_group_kernel(Recurren
     const int s = bid / HK;
     const int hk = bid - s * HK;
     const int slot = a.state_indices[s];
-    if (slot < 0) return;
+    if ((unsigned)slot >= (unsigned)a.num_slots) return;   // padding, or outside the pool
     const int tid = threadIdx.x;
     const int j = (tid & 63) % G;
     const int dv = a.dv, n_rows = grp * dv;

@@ -35,10 +35,14 @@
  *   8 elements (16 bytes); fp32 state pointers are 16-byte aligned.
  * - Sequences are packed back to back.  query_start_loc[s] .. [s+1] is the
  *   token range of sequence s; it must be non-decreasing with
- *   query_start_loc[0] == 0 (device-side preconditions are documented, not
- *   checked).  state_indices[s] selects the state slot of sequence s; a
- *   negative index marks padding: that sequence is skipped, its outputs and
- *   every slot are left untouched.  Slots used in one call must be distinct.
+ *   query_start_loc[0] == 0 and query_start_loc[num_seqs] == num_tokens
+ *   (device-side preconditions: not checked, but the kernels clamp every
+ *   range to [0, num_tokens), so a malformed array gives wrong results,
+ *   never an access outside the buffers).  state_indices[s] selects the
+ *   state slot of sequence s; a negative index marks padding: that sequence
+ *   is skipped, its outputs and every slot are left untouched.  An index at
+ *   or past num_slots is skipped the same way (the kernels check it).  Slots
+ *   used in one call must be distinct.
  *
  * Return values: GDN_OK or a negative gdn_status; gdn_last_error() then
  * describes the failure (thread-local, valid until the thread's next call).
@@ -126,14 +130,20 @@ int gdn_build_conv_chunks(const int32_t *qsl_host, int32_t num_seqs,
  *   state_indices     int32 [num_seqs]
  *   has_initial_state uint8 [num_seqs], or NULL (= every sequence has one)
  *   chunks, n_chunks  descriptors from gdn_build_conv_chunks on the same
- *                     query_start_loc, copied to the device.  Both NULL/0 is a
- *                     valid empty call; exactly one of them set is an error.
+ *                     query_start_loc, copied to the device: the only
+ *                     dispatch, so required whenever num_tokens > 0.  Both
+ *                     NULL/0 is valid only with num_tokens == 0 (the call
+ *                     then enqueues nothing); exactly one of them set is an
+ *                     error.  A descriptor whose seq is not in [0, num_seqs)
+ *                     or whose chunk lies past its sequence is skipped.
  *   y                 bf16 [num_tokens][y_stride]; must not overlap x,
  *                     conv_state, weight or bias
  *
  * Errors: GDN_ERR_INVALID (required pointer NULL, negative count,
- * (chunks == NULL) != (n_chunks == 0), stride < channels, y overlapping x,
- * conv_state, weight or bias, num_slots < 1); GDN_ERR_UNSUPPORTED (width != 4, channels % 8, strides or
+ * (chunks == NULL) != (n_chunks == 0), num_tokens > 0 without descriptors,
+ * fewer than ceil(num_tokens / 8) or more than num_tokens descriptors,
+ * stride < channels, y overlapping x, conv_state, weight or bias,
+ * num_slots < 1); GDN_ERR_UNSUPPORTED (width != 4, channels % 8, strides or
  * pointers off the 16-byte contract); GDN_ERR_HIP (launch failure).
  */
 int gdn_causal_conv1d_varlen(const gdn_bf16 *x, int64_t x_stride,

@@ -21,7 +21,7 @@ import torch
 BF16_MAX_ABS = 2e-2
 BF16_REL_L2 = 5e-3
 STATE_REL_F = 1e-4
-SENTINEL = 0x7FA5          # a quiet-NaN bf16 pattern: "never written"
+SENTINEL = 0x7FE5          # a quiet-NaN bf16 pattern (quiet bit 0x0040 set): "never written"
 
 
 def bf16_half_ulp(ref):

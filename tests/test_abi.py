@@ -95,12 +95,22 @@ def varlen(**kw):
     (dict(xs=8000), INV), (dict(ys=100), INV), (dict(y=X), INV), (dict(y=X + 2 * 8192), INV),
     (dict(y=CS), INV), (dict(y=W, x=Y), INV), (dict(y=B), INV),     # y over conv_state, weight, bias
     (dict(nch=3000), INV), (dict(S=0), INV),
+    (dict(ch=None, nch=0), INV),                 # tokens but no descriptors: nothing would run
+    (dict(nch=255), INV),                        # 255 descriptors cannot cover 2048 tokens
+    (dict(nch=1, T=9, S=1), INV),                # nor one descriptor 9 tokens
     (dict(K=3), UNS), (dict(K=5), UNS), (dict(C=8190, xs=8190, ys=8190), UNS),
     (dict(xs=8196), UNS), (dict(x=X + 2), UNS), (dict(b=B + 8), UNS), (dict(cs=CS + 4), UNS),
 ])
 def test_conv_varlen_validation(kw, code):
     assert varlen(**kw) == code, gdn.lib.gdn_last_error()
     assert gdn.lib.gdn_last_error()
+
+
+def test_conv_varlen_without_tokens_or_descriptors_is_a_no_op():
+    """No tokens and no descriptors: valid, and nothing is enqueued (the
+    fake device addresses are never touched)."""
+    assert varlen(ch=None, nch=0, T=0) == gdn.GDN_OK, gdn.lib.gdn_last_error()
+    assert varlen(ch=None, nch=0, T=0, S=0) == gdn.GDN_OK
 
 
 def update(**kw):
@@ -259,3 +269,4 @@ def test_mixed_both_halves_empty_enqueue_nothing():
     assert mixed(S=0, T=0, B=0, do=Q, o=X) == gdn.GDN_OK
     assert mixed(S=0, T=0, B=0, q=None, o=None, ws=None, x=None, do=None, st=None) == gdn.GDN_OK
     assert mixed(S=0, T=-1, B=0) == INV and mixed(S=3, T=2019, B=-1) == INV
+

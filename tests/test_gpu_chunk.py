@@ -182,3 +182,36 @@ def test_chunk_many_short_sequences_several_rounds():
     o, st, o_ref, st_ref = run_chunk(d)
     check_bf16(o, o_ref, "chunk 32 x 64 o")
     check_state(st, st_ref, d["state"], [int(s) for s in d["state_indices"]])
+
+
+def test_side_stream_without_workspace():
+    """The call on a side stream, its workspace allocated by the binding: the
+    block must stay reserved for that stream's kernels.  The current stream
+    meanwhile allocates a same-size buffer and overwrites it again and again
+    while the side stream's kernels run (they start behind a sleep); if the
+    workspace's memory had been handed out again, the scan would read the
+    overwritten records.  Outputs must equal a call on the current stream
+    bit for bit."""
+    d = synth.mixed_step(0, with_recurrence=True)
+    nd = d["n_dec"]
+    q, k, v = dev(d["q"][nd:]), dev(d["k"][nd:]), dev(d["v"][nd:])
+    g, b = dev(d["g"][nd:]), dev(d["beta"][nd:])
+    idx, qsl, hi = dev(d["state_indices"]), dev(d["qsl"]), dev(d["has_init"])
+    T, HV, dv_ = q.shape[0], d["HV"], d["dv"]
+    o_ref, st_ref = sentinel_like((T, HV, dv_)), dev(d["state"])
+    gdn.gdn_chunk_gated_delta_rule(q, k, v, g, b, st_ref, idx, o_ref, qsl, hi)
+    torch.cuda.synchronize()
+    need = gdn.gdn_chunk_workspace_size(len(d["state_indices"]), T, d["HK"], HV)
+    o, st = sentinel_like((T, HV, dv_)), dev(d["state"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)
+    gdn.gdn_chunk_gated_delta_rule(q, k, v, g, b, st, idx, o, qsl, hi, stream=side)
+    junk = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for i in range(300):
+        junk.fill_(i & 255)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o), bits(o_ref))
+    assert torch.equal(st.view(torch.int32), st_ref.view(torch.int32))

@@ -179,6 +179,35 @@ def test_strided_rows_match_packed():
     assert np.array_equal(y1, y2) and np.array_equal(s1, s2)
 
 
+def test_round_bf16_rounds_doubles_once():
+    """Doubles just off a bf16 tie, closer to it than float32 can resolve:
+    the nearest bf16 is fixed by the side of the tie the value lies on.
+    Rounding through float32 first would land on the tie itself and then
+    round to even, picking the wrong neighbour for half of these values.
+    Expected values come from the construction (the two bf16 neighbours
+    around each tie), not from any rounding routine."""
+    r = np.random.default_rng(3)
+    n = 20000
+    # random finite, normal bf16 values and the next bf16 away from zero
+    exp_bits = r.integers(1, 254, n).astype(np.uint32) << 7
+    man = r.integers(0, 127, n).astype(np.uint32)        # 127 excluded: the neighbour keeps the exponent
+    sign = r.integers(0, 2, n).astype(np.uint32) << 15
+    lo_bits = (sign | exp_bits | man).astype(np.uint16)
+    hi_bits = (lo_bits + 1).astype(np.uint16)            # one ulp further from zero
+    lo = synth.from_bf16(lo_bits).astype(np.float64)
+    hi = synth.from_bf16(hi_bits).astype(np.float64)
+    tie = (lo + hi) / 2                                   # exact in float64
+    # offsets well below half a float32 ulp of the tie, yet nonzero in float64
+    off = np.abs(tie) * 2.0 ** -40
+    above, below = tie + np.sign(tie) * off, tie - np.sign(tie) * off
+    assert np.all(above.astype(np.float32).astype(np.float64) == tie)    # float32 cannot tell them apart
+    assert np.array_equal(oracle.round_bf16(above), hi_bits)
+    assert np.array_equal(oracle.round_bf16(below), lo_bits)
+    # and exactly on the tie: to the neighbour with the even last bit
+    even = np.where(lo_bits % 2 == 0, lo_bits, hi_bits)
+    assert np.array_equal(oracle.round_bf16(tie), even)
+
+
 def test_round_bf16_matches_input_rounding():
     """The oracle's own fp64 -> bf16 rounding agrees with round-to-nearest-even
     done on the float32 bit pattern for values that are exactly float32."""

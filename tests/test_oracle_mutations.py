@@ -36,7 +36,7 @@ def _pins():
             gd.test_single_token_from_zero_closed_form, gd.test_identity_when_beta_zero_alpha_one,
             gd.test_zero_key_only_decays, gd.test_delta_rule_retrieval,
             gd.test_orthonormal_keys_accumulate_outer_products, gd.test_gqa_head_map,
-            gd.test_padding_slot_and_no_initial_state]
+            gd.test_padding_slot_and_no_initial_state, cv.test_round_bf16_rounds_doubles_once]
     pins += [lambda L=L: cv.test_short_sequences_state_carry(L) for L in (0, 1, 2, 3, 5, 9)]
     pins += [lambda n=n, hk=hk, hv=hv: gd.test_dense_brute_force(n, hk, hv)
              for n in (True, False) for (hk, hv) in ((2, 2), (2, 4))]
@@ -71,6 +71,8 @@ MUTATIONS = [
      "for (int32_t j = 0; j < dk; ++j) acc += S[(int64_t)i * dk + j] * qh[j];",
      "for (int32_t j = 0; j < dk; ++j) acc += S[(int64_t)i * dk + j] * kh[j];"),
     ("initial state ignored", "            if (!init)\n", "            if (0)\n"),
+    ("bf16 rounding through float32 first", "const double r = rint(d / ulp) * ulp;",
+     "const double r = rint((double)(float)d / ulp) * ulp;"),
 ]
 
 
