@@ -27,7 +27,10 @@ CONV_WIDTH = 4
 # every entry point declared in include/gdn.h
 EXPORTS = ("gdn_last_error", "gdn_build_conv_chunks", "gdn_causal_conv1d_varlen",
            "gdn_causal_conv1d_update", "gdn_fused_recurrent_decode", "gdn_chunk_gated_delta_rule",
-           "gdn_fused_conv_decode", "gdn_chunk_workspace_size", "gdn_chunk_rule_and_fused_decode")
+           "gdn_fused_conv_decode", "gdn_chunk_workspace_size", "gdn_chunk_rule_and_fused_decode",
+           "gdn_chunk_rule_and_fused_decode_noalloc")
+# bytes of the static device scratch gdn_chunk_rule_and_fused_decode_noalloc uses (gdn.h)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class GDNError(RuntimeError):
@@ -56,6 +59,10 @@ def _bind(path):
                                           i32, i32, i32, i32, i32, i32, f32, i32, P]
     lib.gdn_chunk_rule_and_fused_decode.argtypes = [
         P, i64, P, i64, P, i64, P, P, P, P, P, P, i64, i32, i32, P, ctypes.c_size_t,   # prefill tokens
+        P, i64, P, P, P, i32, P, P, P, P, i64, P, i64, i32, i32,                       # decode rows
+        P, i32, i32, i32, i32, i32, f32, i32, P]                                       # shared
+    lib.gdn_chunk_rule_and_fused_decode_noalloc.argtypes = [
+        P, i64, P, i64, P, i64, P, P, P, P, P, P, i64, i32, i32,                        # prefill tokens
         P, i64, P, P, P, i32, P, P, P, P, i64, P, i64, i32, i32,                       # decode rows
         P, i32, i32, i32, i32, i32, f32, i32, P]                                       # shared
     lib.gdn_chunk_workspace_size.argtypes = [i32, i32, i32, i32]
@@ -466,3 +473,25 @@ def gdn_chunk_rule_and_fused_decode(q, k, v, g, beta, state_indices, o, query_st
                                              float(scale), int(bool(qk_l2norm)), _stream(stream))
     _check(rc, "gdn_chunk_rule_and_fused_decode")
 
+
+def gdn_chunk_rule_and_fused_decode_noalloc(q, k, v, g, beta, state_indices, o, query_start_loc,
+                                            has_initial_state, dec_x, conv_weight, conv_bias, conv_state, dec_g,
+                                            dec_beta, dec_state_indices, dec_o, state, num_k_heads, dec_y=None,
+                                            silu=True, scale=1.0, qk_l2norm=True, stream=None):
+    """gdn_chunk_rule_and_fused_decode with the library's static device
+    scratch (NOALLOC_SCRATCH_BYTES per GPU) as the chunk workspace: neither
+    the library nor this wrapper allocates device memory.  Calls that
+    overlap in time on one GPU race on that scratch; see gdn.h."""
+    named = [("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state_indices", state_indices), ("o", o),
+             ("query_start_loc", query_start_loc), ("has_initial_state", has_initial_state), ("dec_x", dec_x),
+             ("conv_weight", conv_weight), ("conv_bias", conv_bias), ("conv_state", conv_state), ("dec_g", dec_g),
+             ("dec_beta", dec_beta), ("dec_state_indices", dec_state_indices), ("dec_o", dec_o), ("state", state),
+             ("dec_y", dec_y)]
+    T, S, B, HK, dk, HV, dv = _mixed_operands(*[t for _n, t in named[:18]], num_k_heads, dec_y)
+    _on_gpu(named)
+    pre, post = _mixed_args(q, k, v, g, beta, state_indices, o, query_start_loc, has_initial_state, dec_x,
+                            conv_weight, conv_bias, conv_state, dec_g, dec_beta, dec_state_indices, dec_o, state,
+                            num_k_heads, dec_y, silu, S, T, B, HV, dk, dv)
+    rc = lib.gdn_chunk_rule_and_fused_decode_noalloc(*pre, *post, float(scale), int(bool(qk_l2norm)),
+                                                     _stream(stream))
+    _check(rc, "gdn_chunk_rule_and_fused_decode_noalloc")

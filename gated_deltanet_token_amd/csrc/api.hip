@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "gdn.h"
 #include "gdn_internal.h"
 
@@ -422,3 +424,68 @@ GDN_EXPORT int gdn_chunk_rule_and_fused_decode(
                       "chunk and decode launch");
 }
 
+// ---------------------------------------------------------------------------
+// The mixed-step call without a caller workspace, for callers that cannot
+// allocate device memory (code under HIP graph capture, tight serving loops).
+// Its workspace is `scratch`, one static device array: every GPU the library
+// runs on holds its own copy, at its own address, until the process ends.
+// In host code the array's name only stands in for the symbol; the device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// address is ever passed to a kernel.
+// ---------------------------------------------------------------------------
+namespace {
+
+static_assert(GDN_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+__device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];      // device address of `scratch`, per device (set once)
+
+// the current device's copy of `scratch`
+int scratch_on_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(GDN_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(GDN_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GDN_OK;
+}
+
+}  // namespace
+
+GDN_EXPORT int gdn_chunk_rule_and_fused_decode_noalloc(
+    const gdn_bf16 *q, int64_t q_stride, const gdn_bf16 *k, int64_t k_stride, const gdn_bf16 *v, int64_t v_stride,
+    const float *g, const float *beta, const int32_t *query_start_loc, const int32_t *state_indices,
+    const uint8_t *has_initial_state, gdn_bf16 *o, int64_t o_stride, int32_t num_seqs, int32_t num_tokens,
+    const gdn_bf16 *dec_x, int64_t dec_x_stride, const gdn_bf16 *conv_weight, const gdn_bf16 *conv_bias,
+    gdn_bf16 *conv_state, int32_t num_conv_slots, const float *dec_g, const float *dec_beta,
+    const int32_t *dec_state_indices, gdn_bf16 *dec_o, int64_t dec_o_stride, gdn_bf16 *dec_y, int64_t dec_y_stride,
+    int32_t dec_batch, int32_t silu, float *state, int32_t num_slots, int32_t num_k_heads, int32_t num_v_heads,
+    int32_t head_k_dim, int32_t head_v_dim, float scale, int32_t qk_l2norm, void *stream) {
+    void *ws = nullptr;
+    if (num_seqs > 0 && num_tokens > 0 && num_k_heads > 0 && num_v_heads > 0) {
+        const int64_t need = gdn::chunk_workspace_bytes(num_seqs, num_tokens, num_k_heads, num_v_heads);
+        if (need > (int64_t)GDN_NOALLOC_SCRATCH_BYTES)
+            return fail(GDN_ERR_CAPACITY,
+                        "%d tokens in %d sequences need %lld bytes of chunk workspace; the static scratch holds %llu "
+                        "(use gdn_chunk_rule_and_fused_decode with a workspace)",
+                        num_tokens, num_seqs, (long long)need, (unsigned long long)GDN_NOALLOC_SCRATCH_BYTES);
+        const int rc = scratch_on_current_device(&ws);
+        if (rc) return rc;
+    }
+    return gdn_chunk_rule_and_fused_decode(
+        q, q_stride, k, k_stride, v, v_stride, g, beta, query_start_loc, state_indices, has_initial_state, o,
+        o_stride, num_seqs, num_tokens, ws, ws ? (size_t)GDN_NOALLOC_SCRATCH_BYTES : 0, dec_x, dec_x_stride,
+        conv_weight, conv_bias, conv_state, num_conv_slots, dec_g, dec_beta, dec_state_indices, dec_o, dec_o_stride,
+        dec_y, dec_y_stride, dec_batch, silu, state, num_slots, num_k_heads, num_v_heads, head_k_dim, head_v_dim,
+        scale, qk_l2norm, stream);
+}

@@ -23,9 +23,11 @@
  *   rounding is round-to-nearest-even.  Arithmetic is fp32.
  * - Unless marked "host", a pointer is a device pointer (HBM of the current
  *   HIP device).  The caller owns every buffer, scratch workspaces included.
- *   The library never allocates, frees or caches device memory or pointers,
- *   holds no global mutable state and may be called from several threads
- *   (each on its own buffers).
+ *   The library never allocates or frees device memory and caches no caller
+ *   pointers; its only global state is the static scratch of
+ *   gdn_chunk_rule_and_fused_decode_noalloc (and that scratch's per-device
+ *   address).  It may be called from several threads, each on its own
+ *   buffers.
  * - GPU calls validate their arguments on the host, then enqueue kernels on
  *   `stream` (a hipStream_t; NULL = the default stream) and return without
  *   waiting.  A call that returns an error enqueued nothing.
@@ -389,6 +391,55 @@ int gdn_chunk_rule_and_fused_decode(
     const int32_t *query_start_loc, const int32_t *state_indices,
     const uint8_t *has_initial_state, gdn_bf16 *o, int64_t o_stride,
     int32_t num_seqs, int32_t num_tokens, void *workspace, size_t workspace_bytes,
+    /* decode rows */
+    const gdn_bf16 *dec_x, int64_t dec_x_stride,
+    const gdn_bf16 *conv_weight, const gdn_bf16 *conv_bias,
+    gdn_bf16 *conv_state, int32_t num_conv_slots,
+    const float *dec_g, const float *dec_beta, const int32_t *dec_state_indices,
+    gdn_bf16 *dec_o, int64_t dec_o_stride, gdn_bf16 *dec_y, int64_t dec_y_stride,
+    int32_t dec_batch, int32_t silu,
+    /* both */
+    float *state, int32_t num_slots, int32_t num_k_heads, int32_t num_v_heads,
+    int32_t head_k_dim, int32_t head_v_dim, float scale, int32_t qk_l2norm,
+    void *stream);
+
+/* Bytes of the static device scratch gdn_chunk_rule_and_fused_decode_noalloc
+ * uses as its chunk workspace (one copy per GPU). */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * gdn_chunk_rule_and_fused_decode_noalloc -- gdn_chunk_rule_and_fused_decode
+ * without the workspace arguments, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  The chunk workspace is instead a static device array
+ * of GDN_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held
+ * until the process ends.
+ *
+ * Arguments, results and errors are those of gdn_chunk_rule_and_fused_decode
+ * (which it calls with that array as the workspace); results are
+ * bit-identical to it.  The call allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine.  Its first call on a device looks
+ * up that device's copy of the array (hipGetSymbolAddress) and keeps the
+ * address.
+ *
+ * Limit: a prefill half whose gdn_chunk_workspace_size(num_seqs, num_tokens,
+ * num_k_heads, num_v_heads) exceeds GDN_NOALLOC_SCRATCH_BYTES is refused
+ * with GDN_ERR_CAPACITY (at 16 q/k and 32 v heads that is about 70 chunks of
+ * 64 tokens, e.g. 2048 tokens in up to 38 sequences).
+ *
+ * Sharing: every call on one GPU uses that GPU's one array, which keeps what
+ * the last call wrote (nothing in it needs to start cleared: each call
+ * writes every record it reads).  Calls that overlap in time on one GPU --
+ * on different streams or from different threads -- race on the array and
+ * give wrong results; the caller must order them, e.g. on one stream.
+ */
+int gdn_chunk_rule_and_fused_decode_noalloc(
+    /* prefill tokens */
+    const gdn_bf16 *q, int64_t q_stride, const gdn_bf16 *k, int64_t k_stride,
+    const gdn_bf16 *v, int64_t v_stride, const float *g, const float *beta,
+    const int32_t *query_start_loc, const int32_t *state_indices,
+    const uint8_t *has_initial_state, gdn_bf16 *o, int64_t o_stride,
+    int32_t num_seqs, int32_t num_tokens,
     /* decode rows */
     const gdn_bf16 *dec_x, int64_t dec_x_stride,
     const gdn_bf16 *conv_weight, const gdn_bf16 *conv_bias,

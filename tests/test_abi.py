@@ -270,3 +270,42 @@ def test_mixed_both_halves_empty_enqueue_nothing():
     assert mixed(S=0, T=0, B=0, q=None, o=None, ws=None, x=None, do=None, st=None) == gdn.GDN_OK
     assert mixed(S=0, T=-1, B=0) == INV and mixed(S=3, T=2019, B=-1) == INV
 
+
+def noalloc(**kw):
+    a = dict(q=Q, qs=2048, k=K_, ks=2048, v=V, vs=4096, g=G, b=BE, qsl=QSL, idx=IDX, hi=None, o=O, os=4096,
+             S=3, T=2019, x=X, xs=8192, w=W, bias=B, cs=CS, cslots=64, dg=DG, dbe=DBE, didx=DIDX, do=DO, dos=4096,
+             y=None, ys=0, B=32, silu=1, st=ST, slots=64, HK=16, HV=32, dk=128, dv=128, scale=1.0, norm=1)
+    a.update(kw)
+    return gdn.lib.gdn_chunk_rule_and_fused_decode_noalloc(
+        a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["g"], a["b"], a["qsl"], a["idx"], a["hi"], a["o"],
+        a["os"], a["S"], a["T"],
+        a["x"], a["xs"], a["w"], a["bias"], a["cs"], a["cslots"], a["dg"], a["dbe"], a["didx"], a["do"], a["dos"],
+        a["y"], a["ys"], a["B"], a["silu"],
+        a["st"], a["slots"], a["HK"], a["HV"], a["dk"], a["dv"], a["scale"], a["norm"], None)
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    m = re.search(r"#define GDN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == gdn.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_refuses_a_prefill_half_larger_than_its_scratch():
+    """Refused on the host, before the scratch is looked up or anything is
+    enqueued (fake device addresses; no GPU needed)."""
+    assert gdn.gdn_chunk_workspace_size(3, 4500, 16, 32) > gdn.NOALLOC_SCRATCH_BYTES
+    assert noalloc(T=4500) == CAP
+    assert b"static scratch" in gdn.lib.gdn_last_error()
+    assert gdn.gdn_chunk_workspace_size(3, 2019, 16, 32) <= gdn.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=0, T=0, B=0), gdn.GDN_OK),              # both halves empty: nothing to do
+    (dict(S=0, T=0, x=None), INV),                  # the decode half's own checks
+    (dict(S=0, T=0, B=-1), INV),
+    (dict(S=0, T=-1, B=0), INV),
+])
+def test_noalloc_without_a_prefill_half(kw, code):
+    """With no prefill tokens the scratch is not needed and never looked up,
+    so these run on the host alone."""
+    assert noalloc(**kw) == code, gdn.lib.gdn_last_error()
