@@ -31,6 +31,9 @@ CFLAGS = [
     "-Wall", "-Wno-unused-result",
     # no packed-FP32 (v_pk_*_f32) instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs: the chunkwise scan's accumulators
+    # feed vector arithmetic directly, with no accumulator-register copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

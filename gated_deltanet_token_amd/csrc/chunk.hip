@@ -15,7 +15,7 @@
 //  * prep (one workgroup per (chunk, one or two v-heads of a q/k head), all
 //    chunks in parallel): the parts that do not depend on the state --
 //    norms, cumulative decay, T = (I + A)^-1, P_ti = scale exp(L_t - L_i)
-//    (qh_t . kh_i) (i <= t), K^T -- written to the caller's workspace;
+//    (qh_t . kh_i) (i <= t) -- written to the caller's workspace;
 //  * scan (one workgroup per (sequence, v-head, 32 or 64 v rows), serial
 //    over the sequence's chunks, each wave owning 16 v rows): [K;Q] S0^T,
 //    R, U = T R, o = S0 part + P U and S_C^T = G_C S0^T + K^T U', with the
@@ -60,10 +60,6 @@ struct ChunkRec {
     float gC[CT];     // G_C in [0]
 };
 static_assert(sizeof(ChunkRec) % 256 == 0, "record alignment");
-// per (chunk, q/k head): K^T [d][t]
-struct KtRec {
-    __bf16 Kt[DKC][CT];
-};
 
 __device__ __forceinline__ int chunk_count(int len) { return (len + CT - 1) / CT; }
 
@@ -102,11 +98,10 @@ __device__ __forceinline__ void split4(const f32x4 &v, bf16x4 &hi, bf16x4 &lo) {
     lo = __builtin_shufflevector(l01, l23, 0, 1, 2, 3);
 }
 
-__device__ __forceinline__ void st4(__bf16 *p, const bf16x4 &v) { *reinterpret_cast<bf16x4 *>(p) = v; }
-
 // Workspace stores are plain: the scan reads the records right after the
-// prep, and finds them in the caches (streaming stores for T and K^T made
+// prep, and finds them in the caches (streaming stores for the records made
 // the whole call 2-3% slower).  The scan's final state is streaming.
+__device__ __forceinline__ void st4(__bf16 *p, const bf16x4 &v) { *reinterpret_cast<bf16x4 *>(p) = v; }
 __device__ __forceinline__ void st8(__bf16 *p, const bf16x8 &v) { *reinterpret_cast<bf16x8 *>(p) = v; }
 
 // A 64 x 64 lower-triangular fp32 matrix in LDS as its ten 16 x 16 blocks
@@ -216,7 +211,7 @@ struct PrepSmem {
 };
 
 template <int VPW>
-__global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, ChunkRec *recs, KtRec *kts) {
+__global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, ChunkRec *recs) {
     constexpr int NT = NTH * VPW, NW = NT / 64;
     __shared__ PrepSmem<VPW> sm;
     const int HV = a.num_v_heads, NP = HV / VPW;
@@ -302,19 +297,6 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
         rec->u2f[t] = expf(lamC - lam) * rk;
         rec->gC[t] = expf(lamC);
     }
-    // K^T for the scan (once per q/k head): NT / 128 threads per dim d, each
-    // CT / (NT / 128) consecutive tokens
-    if ((h0 % grp) == 0) {
-        constexpr int PARTS = NT / DKC, TPT = CT / PARTS;
-        const int d = tid / PARTS, part = tid % PARTS;
-        bf16x8 col[TPT / 8];
-#pragma unroll
-        for (int jj = 0; jj < TPT; ++jj) col[jj >> 3][jj & 7] = sm.u.K[TPT * part + jj][d];
-        __bf16 *dst = &kts[(int64_t)gch * a.num_k_heads + hk].Kt[d][TPT * part];
-#pragma unroll
-        for (int m = 0; m < TPT / 8; ++m) st8(dst + 8 * m, col[m]);
-    }
-
     // ---- stage 1: the ten lower-triangular tiles (t-tile bt, i-tile bc) of
     // K K^T and K Q^T, round-robin over the waves, laid out so each lane holds
     // 4 consecutive i of one row t; per v-head, A (fp32) into its LDS block and
@@ -454,14 +436,19 @@ __device__ __forceinline__ int pstart(int c8) {       // c8: first column of 8, 
 }
 template <int NW>
 struct RowScanSmem {
-    alignas(16) __bf16 K[CT][RLDK];                  // [t][d]
+    alignas(16) __bf16 K[CT][RLDK];                  // [t][d]; also read transposed as K^T
     alignas(16) __bf16 Q[CT][RLDK];
-    alignas(16) __bf16 Kt[DKC][RLDT];                // [d][t]
     alignas(16) __bf16 Th[CT][RLDT];                 // [t][i]
     alignas(16) __bf16 Tl[CT][RLDT];
     alignas(16) __bf16 Ph[CT][RLDT];
     alignas(16) __bf16 Pl[CT][RLDT];
-    alignas(16) __bf16 V[CT][16 * NW + 8];           // [t][r], this workgroup's rows
+    // [t][r], this workgroup's rows.  The 64-row form's LDS (~82 KB) keeps one
+    // workgroup per CU: with rows padded by 4 instead of 8 it fits in 80 KB,
+    // and in the mixed-step grid decode units then share CUs with scan
+    // workgroups, which made the grid ~3% slower (their memory traffic slows
+    // the scan's operand fetches; a higher wave priority for the scan did not
+    // help).
+    alignas(16) __bf16 V[CT][16 * NW + 8];
     alignas(16) float sc[5][CT];                     // beta, bgr, sqg, u2f, G_C
 };
 
@@ -471,6 +458,27 @@ struct RowScanSmem {
 // e >= 4 -- in the permuted block layout, the 8 elements from k0 + 8 (l / 16)
 __device__ __forceinline__ bf16x8 afrag(const __bf16 *base, int ld, int r0, int k0, int lane) {
     return *reinterpret_cast<const bf16x8 *>(base + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+}
+
+// The same A-side fragment of K^T (rows d0 .. d0 + 15, contraction over the
+// tokens t0 + 4 (l / 16) + e and t0 + 16 + 4 (l / 16) + e - 4), read straight
+// from the staged K tile [t][d] with two gfx950 LDS transpose reads
+// (ds_read_b64_tr_b16).  Within each group of 16 lanes such a read gives
+// lane j, as its element e, element j % 4 of the 8-byte piece whose address
+// lane 4 e + j / 4 of the group supplies (checked on the GPU with an
+// in-bounds probe).  So lane 4 e + q of group g points at the four
+// consecutive d0 + 4 q .. d0 + 4 q + 3 of token row t0 + 4 g + e; four
+// consecutive columns stay contiguous in the permuted block layout.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 ktfrag(const __bf16 *K, int d0, int t0, int lane) {
+    const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+    const int d = d0 + 4 * q;                            // a multiple of 4
+    const int col = (d & ~31) + 8 * ((d >> 2) & 3) + 4 * ((d >> 4) & 1);
+    const __bf16 *p = K + (t0 + 4 * g + e) * RLDK + col;
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 16 * RLDK));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // B-side fragment (hi and lo bf16 parts) from two accumulator tiles stacked
@@ -486,10 +494,10 @@ __device__ __forceinline__ void bsplit(const f32x4 &x0, const f32x4 &x1, bf16x8 
 template <int NW>
 struct RowStage {
     static constexpr int NT = 64 * NW, DVB = 16 * NW;
-    static constexpr int NK = CT * DKC / 8 / NT;          // K (and Q, K^T) vectors per thread
+    static constexpr int NK = CT * DKC / 8 / NT;          // K (and Q) vectors per thread
     static constexpr int NTP = 4 * NBLK16 * 32 / NT;      // 16-byte pieces of the T and P blocks per thread
     static constexpr int NV = CT * DVB / 8 / NT;          // v vectors per thread
-    uint4 k[NK], q[NK], kt[NK];
+    uint4 k[NK], q[NK];
     uint4 tp[NTP];
     uint4 v[NV];
     uint4 sc;                                          // threads < 80: 4 scalars of one of 5 arrays
@@ -502,7 +510,7 @@ struct RowStage {
 // instance shared by two kernels, hipcc 7.2 scheduled the scan kernel's loop
 // with 26 more AGPR moves.
 template <int NW, int TAG = 0>
-__device__ __forceinline__ void scan_rows_unit(const RecurrentArgs &a, const ChunkRec *recs, const KtRec *kts,
+__device__ __forceinline__ void scan_rows_unit(const RecurrentArgs &a, const ChunkRec *recs,
                                                int n_vblocks, int work, RowScanSmem<NW> &sm) {
     using St = RowStage<NW>;
     constexpr int NT = St::NT, DVB = St::DVB;
@@ -554,14 +562,6 @@ __device__ __forceinline__ void scan_rows_unit(const RecurrentArgs &a, const Chu
             st.q[j] = *reinterpret_cast<const uint4 *>(a.q + row * a.q_stride + hk * DKC + c);
         }
     };
-    auto fetch_kt = [&](St &st, int gch) {
-        const KtRec *kt = kts + (int64_t)gch * a.num_k_heads + hk;
-#pragma unroll
-        for (int j = 0; j < St::NK; ++j) {
-            const int idx = tid + NT * j, d = idx >> 3, ct = (idx & 7) * 8;
-            st.kt[j] = *reinterpret_cast<const uint4 *>(&kt->Kt[d][ct]);
-        }
-    };
     // T and P: the record's ten blocks of each of the four matrices are
     // 1280 consecutive 16-byte pieces
     auto fetch_t = [&](St &st, int gch) {
@@ -593,8 +593,6 @@ __device__ __forceinline__ void scan_rows_unit(const RecurrentArgs &a, const Chu
             const int idx = tid + NT * j, t = idx >> 4, c = (idx & 15) * 8;
             st16(sm.K[t], c, st.k[j]);
             st16(sm.Q[t], c, st.q[j]);
-            const int d = idx >> 3, ct = (idx & 7) * 8;
-            st16(sm.Kt[d], ct, st.kt[j]);
         }
 #pragma unroll
         for (int j = 0; j < St::NTP; ++j) {
@@ -626,7 +624,6 @@ __device__ __forceinline__ void scan_rows_unit(const RecurrentArgs &a, const Chu
     {
         const int n0 = min(CT, t_end - t_begin);
         fetch_kq(st, t_begin, n0);
-        fetch_kt(st, gch0);
         fetch_t(st, gch0);
         fetch_pv(st, t_begin, n0, gch0);
     }
@@ -679,7 +676,6 @@ __device__ __forceinline__ void scan_rows_unit(const RecurrentArgs &a, const Chu
         }
         // ---- U = T R (T lower triangular: token tile tt needs blocks ib <= tt / 2); U' = u2f U
         f32x4 U[4], U2[4];
-        fetch_kt(st, g_next);
         {
             bf16x8 rh[2], rl[2];
             bsplit(R[0], R[1], rh[0], rl[0]);
@@ -740,7 +736,7 @@ __device__ __forceinline__ void scan_rows_unit(const RecurrentArgs &a, const Chu
                 f32x4 acc = S[dt] * g_c;
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) {
-                    const bf16x8 ka = afrag(&sm.Kt[0][0], RLDT, 16 * dt, 32 * tb, lane);
+                    const bf16x8 ka = ktfrag(&sm.K[0][0], 16 * dt, 32 * tb, lane);
                     acc = mma(ka, vh[tb], acc);
                     acc = mma(ka, vl[tb], acc);
                 }
@@ -759,9 +755,9 @@ __device__ __forceinline__ void scan_rows_unit(const RecurrentArgs &a, const Chu
 
 template <int NW>
 __global__ __launch_bounds__(64 * NW, 1) void chunk_scan_rows_kernel(RecurrentArgs a, const ChunkRec *recs,
-                                                                     const KtRec *kts, int n_vblocks) {
+                                                                     int n_vblocks) {
     __shared__ RowScanSmem<NW> sm;
-    scan_rows_unit<NW>(a, recs, kts, n_vblocks, xcd_contiguous(blockIdx.x, gridDim.x), sm);
+    scan_rows_unit<NW>(a, recs, n_vblocks, xcd_contiguous(blockIdx.x, gridDim.x), sm);
 }
 
 // The scan and a batch of fused decode units (fused_unit.h) in one grid, for
@@ -781,13 +777,13 @@ static_assert(sizeof(RowScanSmem<4>) >= kMaxGroupChannels * sizeof(uint16_t),
               "a decode unit's conv output fits in the scan's LDS");
 
 __global__ __launch_bounds__(kMixedThreads, 1) void chunk_scan_decode_kernel(RecurrentArgs a, const ChunkRec *recs,
-                                                                           const KtRec *kts, int n_vblocks,
+                                                                           int n_vblocks,
                                                                            int n_scan, int n_scan_pad,
                                                                            FusedDecodeArgs f, int n_dec) {
     __shared__ RowScanSmem<4> sm;
     const int bid = blockIdx.x;
     if (bid < n_scan_pad) {
-        if (bid < n_scan) scan_rows_unit<4, 1>(a, recs, kts, n_vblocks, xcd_contiguous(bid, n_scan), sm);
+        if (bid < n_scan) scan_rows_unit<4, 1>(a, recs, n_vblocks, xcd_contiguous(bid, n_scan), sm);
     } else {
         // n_scan_pad is a multiple of the XCD count: bid - n_scan_pad stays on bid's XCD
         fused_decode_unit<DKC, kFusedRows>(f, xcd_contiguous(bid - n_scan_pad, n_dec),
@@ -803,14 +799,14 @@ int64_t chunk_max_chunks(int num_seqs, int num_tokens) {
 
 int64_t chunk_workspace_bytes(int num_seqs, int num_tokens, int num_k_heads, int num_v_heads) {
     const int64_t mc = chunk_max_chunks(num_seqs, num_tokens);
-    return mc * ((int64_t)num_v_heads * (int64_t)sizeof(ChunkRec) + (int64_t)num_k_heads * (int64_t)sizeof(KtRec));
+    (void)num_k_heads;
+    return mc * (int64_t)num_v_heads * (int64_t)sizeof(ChunkRec);
 }
 
 namespace {
 
 struct ChunkLaunch {
     ChunkRec *recs;
-    KtRec *kts;
     long long prep_blocks, scan_blocks;
     int nvb;
     bool wide;
@@ -820,8 +816,6 @@ ChunkLaunch chunk_launch(const RecurrentArgs &a, void *workspace, int num_tokens
     ChunkLaunch c;
     const int64_t mc = chunk_max_chunks(a.num_seqs, num_tokens);
     c.recs = reinterpret_cast<ChunkRec *>(workspace);
-    c.kts = reinterpret_cast<KtRec *>(reinterpret_cast<char *>(workspace) +
-                                      mc * a.num_v_heads * (int64_t)sizeof(ChunkRec));
     c.prep_blocks = mc * a.num_v_heads;
     // 64 v rows (four waves) per workgroup whenever head_v_dim allows: each
     // chunk's operands then serve twice the rows, which measured faster at
@@ -837,20 +831,19 @@ hipError_t launch_prep(const RecurrentArgs &a, const ChunkLaunch &c, hipStream_t
     // two v-heads per prep workgroup whenever the v-heads of a q/k head pair up
     if ((a.num_v_heads / a.num_k_heads) % 2 == 0)
         hipLaunchKernelGGL(chunk_prep_kernel<2>, dim3((unsigned)(c.prep_blocks / 2)), dim3(2 * NTH), 0, stream, a,
-                           c.recs, c.kts);
+                           c.recs);
     else
-        hipLaunchKernelGGL(chunk_prep_kernel<1>, dim3((unsigned)c.prep_blocks), dim3(NTH), 0, stream, a, c.recs,
-                           c.kts);
+        hipLaunchKernelGGL(chunk_prep_kernel<1>, dim3((unsigned)c.prep_blocks), dim3(NTH), 0, stream, a, c.recs);
     return hipGetLastError();
 }
 
 hipError_t launch_scan(const RecurrentArgs &a, const ChunkLaunch &c, hipStream_t stream) {
     if (c.wide)
         hipLaunchKernelGGL(chunk_scan_rows_kernel<4>, dim3((unsigned)c.scan_blocks), dim3(256), 0, stream, a, c.recs,
-                           c.kts, c.nvb);
+                           c.nvb);
     else
         hipLaunchKernelGGL(chunk_scan_rows_kernel<2>, dim3((unsigned)c.scan_blocks), dim3(128), 0, stream, a, c.recs,
-                           c.kts, c.nvb);
+                           c.nvb);
     return hipGetLastError();
 }
 
@@ -883,7 +876,7 @@ hipError_t launch_chunk_and_decode(const RecurrentArgs &a, void *workspace, int 
         return launch_fused_conv_decode(f, stream);
     }
     hipLaunchKernelGGL(chunk_scan_decode_kernel, dim3((unsigned)(n_scan_pad + n_dec)), dim3(kMixedThreads), 0, stream,
-                       a, c.recs, c.kts, c.nvb, (int)c.scan_blocks, (int)n_scan_pad, f, (int)n_dec);
+                       a, c.recs, c.nvb, (int)c.scan_blocks, (int)n_scan_pad, f, (int)n_dec);
     return hipGetLastError();
 }
 

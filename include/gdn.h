@@ -251,7 +251,7 @@ int gdn_fused_recurrent_decode(const gdn_bf16 *q, int64_t q_stride,
  *
  * Two kernels run on `stream`: one prepares, for every (64-token chunk,
  * v-head) in parallel, the parts that do not depend on the state (the
- * inverse of I + A, the masked decayed Q K^T, per-token factors, K^T) in
+ * inverse of I + A, the masked decayed Q K^T, per-token factors) in
  * `workspace`; the second walks each sequence's chunks in order.
  *
  * Arguments, layouts, state semantics and errors are those of
@@ -424,8 +424,8 @@ int gdn_chunk_rule_and_fused_decode(
  *
  * Limit: a prefill half whose gdn_chunk_workspace_size(num_seqs, num_tokens,
  * num_k_heads, num_v_heads) exceeds GDN_NOALLOC_SCRATCH_BYTES is refused
- * with GDN_ERR_CAPACITY (at 16 q/k and 32 v heads that is about 70 chunks of
- * 64 tokens, e.g. 2048 tokens in up to 38 sequences).
+ * with GDN_ERR_CAPACITY (at 16 q/k and 32 v heads that is about 96 chunks of
+ * 64 tokens, e.g. 2048 tokens in up to 64 sequences).
  *
  * Sharing: every call on one GPU uses that GPU's one array, which keeps what
  * the last call wrote (nothing in it needs to start cleared: each call

@@ -49,11 +49,12 @@ def test_calls_in_a_row_match_the_workspace_call():
 
 
 def test_refuses_a_prefill_half_larger_than_the_scratch():
-    """4500 tokens at 16 q/k and 32 v heads need more chunk workspace than
-    the scratch holds: refused before anything is enqueued."""
-    need = gdn.gdn_chunk_workspace_size(3, 4500, 16, 32)
-    assert need > gdn.NOALLOC_SCRATCH_BYTES
-    d = make_case(4, [1500, 1500, 1500], 2, 16, 32, 128, 64, [0, 0, 0])
+    """Three sequences at 16 q/k and 32 v heads with just more tokens than
+    the scratch's chunk records cover: refused before anything is enqueued."""
+    T = 64
+    while gdn.gdn_chunk_workspace_size(3, T, 16, 32) <= gdn.NOALLOC_SCRATCH_BYTES:
+        T += 64
+    d = make_case(4, [T // 3, T // 3, T - 2 * (T // 3)], 2, 16, 32, 128, 64, [0, 0, 0])
     t = operands(d)
     with pytest.raises(gdn.GDNError) as e:
         gdn.gdn_chunk_rule_and_fused_decode_noalloc(t["q"], t["k"], t["v"], t["g"], t["beta"], t["idx"], t["o"],
