@@ -26,19 +26,32 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_oracle.c")
 _LIB = os.path.join(_HERE, "libgdn_oracle.so")
+# the same source built with OpenMP: only the benchmark's multi-core CPU
+# baseline loads it (same results; independent iterations on several threads)
+_LIB_OMP = os.path.join(_HERE, "libgdn_oracle_omp.so")
+_FLAGS = ["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall",
+          "-Wextra"]
 
 _lib = None
 
 
+def _compile(lib, extra, force):
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+        tmp = lib + ".tmp%d" % os.getpid()
+        subprocess.check_call(_FLAGS + extra + ["-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, lib)
+    return lib
+
+
 def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (IEEE double, no FMA contraction)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(
-            ["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
-             "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+    """Compile the oracle with gcc (IEEE double, no FMA contraction), serial:
+    its OpenMP pragmas are ignored."""
+    return _compile(_LIB, ["-Wno-unknown-pragmas"], force)
+
+
+def build_omp(force: bool = False) -> str:
+    """The same oracle compiled with OpenMP (for the multi-core CPU baseline)."""
+    return _compile(_LIB_OMP, ["-fopenmp"], force)
 
 
 def bind(path: str):

@@ -7,6 +7,13 @@
  * the smoke check and the CPU-baseline leg of the benchmark may load it.
  * It shares no code, header, table or helper with the HIP library.
  *
+ * Serial as compiled for the tests.  The OpenMP pragmas mark loops whose
+ * iterations are independent (channels of the conv, (sequence, v-head)
+ * pairs of the recurrence); built with -fopenmp for the benchmark's
+ * multi-core CPU baseline they run those iterations on several threads,
+ * each iteration doing exactly the same operations in the same order, so
+ * both builds give bit-identical results.
+ *
  * Every function reads bf16 inputs exactly (bf16 -> double is exact), does
  * all arithmetic in double, and returns double results unrounded, so the
  * comparison with the GPU measures the GPU's error alone.  The state pools
@@ -107,7 +114,6 @@ void oracle_causal_conv1d_varlen(const uint16_t *x, int64_t x_stride,
 {
     (void)num_slots;
     const int32_t C = channels, K = width;
-    uint16_t *e = NULL;            /* one channel's window, bf16 bits */
     for (int32_t s = 0; s < num_seqs; ++s) {
         const int64_t a = qsl[s];
         const int64_t L = (int64_t)qsl[s + 1] - a;
@@ -115,7 +121,11 @@ void oracle_causal_conv1d_varlen(const uint16_t *x, int64_t x_stride,
         if (slot < 0 || L <= 0) continue;
         const int init = has_init ? has_init[s] != 0 : 1;
         uint16_t *st = conv_state + (int64_t)slot * (K - 1) * C;
-        e = (uint16_t *)realloc(e, sizeof(uint16_t) * (size_t)(K - 1 + L));
+#pragma omp parallel
+        {
+        /* one channel's window, bf16 bits (one buffer per thread) */
+        uint16_t *e = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(K - 1 + L));
+#pragma omp for schedule(static)
         for (int32_t c = 0; c < C; ++c) {
             /* build the window for this channel: carried state, then inputs */
             for (int32_t i = 0; i < K - 1; ++i)
@@ -133,8 +143,9 @@ void oracle_causal_conv1d_varlen(const uint16_t *x, int64_t x_stride,
             for (int32_t i = 0; i < K - 1; ++i)
                 st[(int64_t)i * C + c] = e[L + i];
         }
+        free(e);
+        }
     }
-    free(e);
 }
 
 /*
@@ -158,6 +169,7 @@ void oracle_causal_conv1d_update(const uint16_t *x, int64_t x_stride,
         if (slot < 0) continue;
         uint16_t *st = conv_state + (int64_t)slot * (K - 1) * C;
         const uint16_t *xb = x + (int64_t)b * x_stride;
+#pragma omp parallel for schedule(static)
         for (int32_t c = 0; c < C; ++c) {
             double z = bias ? bf16_bits_to_double(bias[c]) : 0.0;
             for (int32_t j = 0; j < K - 1; ++j)
@@ -207,16 +219,21 @@ void oracle_gated_delta_rule(const uint16_t *q, int64_t q_stride,
 {
     (void)num_slots;
     const int32_t HV = num_v_heads, group = num_v_heads / num_k_heads;
+#pragma omp parallel
+    {
+    /* per-thread scratch: the normalized q and k rows, and S k */
     double *qh = (double *)malloc(sizeof(double) * (size_t)dk);
     double *kh = (double *)malloc(sizeof(double) * (size_t)dk);
     double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+#pragma omp for collapse(2) schedule(dynamic)
     for (int32_t s = 0; s < num_seqs; ++s) {
+        for (int32_t h = 0; h < HV; ++h) {
         const int64_t t0 = qsl ? qsl[s] : s;
         const int64_t t1 = qsl ? qsl[s + 1] : s + 1;
         const int32_t slot = state_indices[s];
         if (slot < 0 || t1 <= t0) continue;
         const int init = has_init ? has_init[s] != 0 : 1;
-        for (int32_t h = 0; h < HV; ++h) {
+        {
             const int32_t hk = h / group;
             double *S = state + ((int64_t)slot * HV + h) * dv * dk;
             if (!init)
@@ -264,10 +281,12 @@ void oracle_gated_delta_rule(const uint16_t *q, int64_t q_stride,
                 }
             }
         }
+        }
     }
     free(qh);
     free(kh);
     free(u);
+    }
 }
 
 /*
