@@ -26,10 +26,18 @@ layers / wall time).  ``roofline`` is for the kernel with the largest share
 of GPU time; its average launch duration comes from HIP events recorded on
 the launch stream inside the timed region: one pair around every run of
 several consecutive launches of that kernel and around every seventh
-one-launch run, the latter weighted, which estimates the kernel's total time
-(each recorded event idles the stream for ~5 us on this GPU; bracketing every
-run cost ~2% of the measured throughput).  ``cpu_baseline`` is the fp64 oracle timed on this host on a
-bounded sample of the same workload.
+one-launch run, the latter weighted, which estimates the kernel's total time.
+Each recorded event idles the stream for a few microseconds on this GPU; that
+cost is measured in the same process (fixed-length spin kernels with and
+without an event pair around each) and subtracted from every bracketed span,
+here and in the per-kernel figures (``kernels``).  ``isolated`` times each
+call alone at its c32 shape with HBM-resident operands, beside a plain copy
+(conv) and an in-place read-modify-write (decode) of the same bytes as
+measured ceilings.  ``cpu_baseline`` is the fp64 oracle timed on this host on
+a bounded sample of the same workload, serial on one core and (``multicore``)
+the same source built with OpenMP on every core, each sample taken half
+before and half after the GPU's timed region.  ``context`` carries the pages'
+own figures (another GPU, a whole engine): context only.
 """
 from __future__ import annotations
 
@@ -54,6 +62,22 @@ ROOFLINE_STRIDE = 7             # every 7th one-launch run of the dominant kerne
 SLOTS = 64
 BUDGET = 2048
 
+# The pages' own figures for this path, carried beside the results as
+# context only: a different GPU and a whole serving engine, not a target.
+PAGES_CONTEXT = {
+    "hardware": "RTX 5070 Ti (sm_120), whole Qwen3.5-4B BF16 engine, c32 workload (128 requests, 1024 in / 128 out, "
+                "concurrency 32, 2048-token budget)",
+    "causal_conv_gpu_time_ms": {"whole_sequence_dispatch": 720.2, "exact_8_token_chunks": 234.4,
+                                "vllm_triton_kernel": 145.4,
+                                "source": 'page "perf(gdn): dispatch exact causal-conv chunks", section "Speed '
+                                          'claims"; vLLM figure: page "RTX 5070 Ti: close Qwen3.5-4B TTFT, TPOT, '
+                                          'and VRAM gaps vs vLLM", section "Existing evidence"'},
+    "end_to_end_tokens_per_s": {"before": 6587.66, "after": 6727.35,
+                                "source": 'page "perf(gdn): dispatch exact causal-conv chunks", section "Speed '
+                                          'claims" (whole model, input + output tokens, profiled run)'},
+    "note": "sums over a whole served run on another GPU; no per-kernel time or bandwidth is given on the pages",
+}
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -62,7 +86,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample-requests", type=int, default=14)
+    ap.add_argument("--cpu-sample-requests", type=int, default=14,
+                    help="requests timed through the serial oracle (one core)")
+    ap.add_argument("--cpu-multicore-requests", type=int, default=48,
+                    help="requests timed through the OpenMP build of the oracle (every core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-isolated", action="store_true",
                     help="skip the per-call measurements at the c32 shapes with HBM-only operands")
@@ -188,7 +215,13 @@ def isolated(seed, reps=64):
         if rc != 0:
             raise RuntimeError("%s: %s" % (what, lib.gdn_last_error().decode()))
 
-    def timed(calls):
+    # the reference copy kernels for the ceilings (their own library)
+    ceil = ctypes.CDLL(os.path.join(ROOT, "gated_deltanet_token_amd", "ceiling", "libgdn_ceiling.so"))
+    ceil.ceiling_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                         ctypes.c_void_p]
+    ceil.ceiling_stream_rmw.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+
+    def timed(calls, reps=reps):
         for c in calls:
             c()
         torch.cuda.synchronize()
@@ -226,6 +259,16 @@ def isolated(seed, reps=64):
         for x, y in sets]
     out["conv_varlen"] = entry(timed(calls), bytes_conv_varlen(T2, 2, 0, len(ch2)),
                                shape="2 x 1024 tokens, 8192 channels, 256 descriptors", buffer_sets=len(sets))
+    # what HBM allows for these bytes: a plain streaming copy of x into y
+    # (the same buffers, the same rotation)
+    nb_copy = 2 * T2 * C * 2
+    us_copy, u_copy = min((timed([lambda x=x, y=y: check(ceil.ceiling_stream_copy(
+        x.data_ptr(), y.data_ptr(), nb_copy // 2, u, sptr), "ceiling copy") for x, y in sets]), u) for u in (1, 4, 16))
+    out["conv_varlen"]["ceiling"] = {
+        "kind": "streaming device copy of the same bytes (%.1f MB in + %.1f MB out, 16-byte nontemporal loads and "
+                "stores, %d per lane: the fastest of 1, 4, 16)" % (nb_copy / 2e6, nb_copy / 2e6, u_copy),
+        "avg_launch_us": us_copy, "gb_per_s": nb_copy / us_copy / 1e3, "hbm_frac": nb_copy / us_copy / 1e3 / HBM_PEAK_GBS}
+    out["conv_varlen"]["frac_of_ceiling"] = out["conv_varlen"]["gb_per_s"] / out["conv_varlen"]["ceiling"]["gb_per_s"]
     del sets, calls
 
     # A2 + A3 at the decode shape: 32 sequences, 16 q/k heads, 32 v heads, d = 128
@@ -247,6 +290,17 @@ def isolated(seed, reps=64):
     out["fused_decode"] = entry(timed(calls), bytes_fused_decode(B), flops_recurrent(B),
                                 shape="32 sequences x 1 token: conv update on 8192 channels + gated delta rule, "
                                       "16 q/k heads, 32 v heads, d 128", buffer_sets=len(pools))
+    # what HBM allows for the state traffic: a streaming in-place
+    # read-modify-write of 32 slots' worth of fp32 state, in the same pools
+    n_rmw = B * HV * D * D
+    nb_rmw = 2 * n_rmw * 4
+    us_rmw, u_rmw = min((timed([lambda p=p: check(ceil.ceiling_stream_rmw(p["state"].data_ptr(), nb_rmw // 2, u, sptr),
+                                                  "ceiling rmw") for p in pools]), u) for u in (1, 4, 16))
+    out["fused_decode"]["ceiling"] = {
+        "kind": "streaming in-place read-modify-write of %.1f MB of fp32 (read and written once, %d 16-byte "
+                "accesses per lane: the fastest of 1, 4, 16)" % (nb_rmw / 2e6, u_rmw),
+        "avg_launch_us": us_rmw, "gb_per_s": nb_rmw / us_rmw / 1e3, "hbm_frac": nb_rmw / us_rmw / 1e3 / HBM_PEAK_GBS}
+    out["fused_decode"]["frac_of_ceiling"] = out["fused_decode"]["gb_per_s"] / out["fused_decode"]["ceiling"]["gb_per_s"]
     calls = [lambda p=p: check(lib.gdn_fused_recurrent_decode(
         p["q"].data_ptr(), HK * D, p["k"].data_ptr(), HK * D, p["v"].data_ptr(), HV * D, g.data_ptr(),
         beta.data_ptr(), p["state"].data_ptr(), SLOTS, None, idx_d.data_ptr(), None, p["o"].data_ptr(), HV * D,
@@ -283,6 +337,17 @@ def isolated(seed, reps=64):
                                          % "+".join(str(x) for x in lens),
                                    buffer_sets=len(sets), tokens_per_s=T3 / us * 1e6,
                                    bound="latency (serial over 64-token chunks)")
+    # the same tokens through the token-by-token form (gdn_fused_recurrent_decode
+    # with query_start_loc): the state stays in registers across a sequence's
+    # tokens, each token a serial step
+    calls = [lambda y=y, st=st, o=o: check(lib.gdn_fused_recurrent_decode(
+        y.data_ptr(), C, y.data_ptr() + HK * D * 2, C, y.data_ptr() + 2 * HK * D * 2, C, g3.data_ptr(),
+        b3.data_ptr(), st.data_ptr(), SLOTS, qsl3.data_ptr(), idx3.data_ptr(), hi3.data_ptr(), o.data_ptr(), HV * D,
+        3, T3, HK, HV, D, D, f1, 1, sptr), "recurrent_token_loop") for y, st, o in sets]
+    us_tl = timed(calls, reps=20)
+    out["recurrent_token_loop"] = entry(us_tl, bytes_recurrent(T3, 1, 3), flops_recurrent(T3),
+                                        shape="the same 3 prefill chunks, token by token", buffer_sets=len(sets),
+                                        tokens_per_s=T3 / us_tl * 1e6, bound="latency (serial over tokens)")
 
     # the mixed step's recurrence as one call (gdn_chunk_rule_and_fused_decode):
     # the same prefill chunks and 29 decode rows on other slots of the same pool,
@@ -319,25 +384,83 @@ def isolated(seed, reps=64):
     return out
 
 
-def cpu_baseline(seed, n_req, seq_len):
-    import oracle
-    import synth
-    w, b = synth.trace_layer_weights(seed, 0)
-    elapsed = 0.0
-    for r in range(n_req):
-        x, g, beta = synth.trace_request_inputs(seed, 0, r, seq_len)
-        t0 = time.perf_counter()
-        y, _ = oracle.causal_conv1d_varlen(x, w, b, np.zeros((1, 3, C), np.uint16), [0, seq_len], [0], [0])
-        yb = oracle.round_bf16(y)
-        q = yb[:, :HK * D].reshape(seq_len, HK, D)
-        k = yb[:, HK * D:2 * HK * D].reshape(seq_len, HK, D)
-        v = yb[:, 2 * HK * D:].reshape(seq_len, HV, D)
-        oracle.gated_delta_rule(q, k, v, g, beta, np.zeros((1, HV, D, D)), [0], [0, seq_len], [0], 1.0, True)
-        elapsed += time.perf_counter() - t0
-    return {"value": n_req * seq_len / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "%d of the 128 requests, %d tokens each (1024 prompt + 127 decode forwards), "
-                      "one GDN layer, whole-sequence oracle passes (conv, bf16 rounding, gated delta "
-                      "rule); serial C in fp64; %.1f s" % (n_req, seq_len, elapsed)}
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class CpuBaseline:
+    """The fp64 oracle timed on this host over whole requests of the trace
+    (one GDN layer: conv, bf16 rounding, gated delta rule per request).  Two
+    legs: the serial oracle on one core, and the same source built with
+    OpenMP on every core in sched_getaffinity (independent conv channels and
+    (sequence, v-head) pairs on separate threads, identical results).  Each
+    leg's sample is taken in two halves, one before and one after the GPU's
+    timed region (the pages' order-alternated A/B practice)."""
+
+    def __init__(self, seed, seq_len, n_serial, n_multi):
+        import ctypes as ct
+        import oracle
+        self.oracle, self.seed, self.seq_len = oracle, seed, seq_len
+        self.w, self.b = None, None
+        self.serial = oracle._load()
+        self.cores = len(os.sched_getaffinity(0))
+        self.omp = oracle.bind(oracle.build_omp())
+        ct.CDLL("libgomp.so.1").omp_set_num_threads(self.cores)
+        self.reqs = {"serial": list(range(n_serial)), "multi": list(range(n_serial, n_serial + n_multi))}
+        self.time = {"serial": 0.0, "multi": 0.0}
+        self.done = {"serial": 0, "multi": 0}
+
+    def _one(self, lib, r):
+        import synth
+        o = self.oracle
+        if self.w is None:
+            self.w, self.b = synth.trace_layer_weights(self.seed, 0)
+        L = self.seq_len
+        x, g, beta = synth.trace_request_inputs(self.seed, 0, r, L)
+        saved = o._lib
+        o._lib = lib
+        try:
+            t0 = time.perf_counter()
+            y, _ = o.causal_conv1d_varlen(x, self.w, self.b, np.zeros((1, 3, C), np.uint16), [0, L], [0], [0])
+            yb = o.round_bf16(y)
+            o.gated_delta_rule(yb[:, :HK * D].reshape(L, HK, D), yb[:, HK * D:2 * HK * D].reshape(L, HK, D),
+                               yb[:, 2 * HK * D:].reshape(L, HV, D), g, beta, np.zeros((1, HV, D, D)), [0], [0, L],
+                               [0], 1.0, True)
+            return time.perf_counter() - t0
+        finally:
+            o._lib = saved
+
+    def half(self, which):
+        """Time the first (which=0) or second half of each leg's sample."""
+        for leg, lib in (("serial", self.serial), ("multi", self.omp)):
+            rs = self.reqs[leg]
+            part = rs[:len(rs) // 2] if which == 0 else rs[len(rs) // 2:]
+            for r in part:
+                self.time[leg] += self._one(lib, r)
+                self.done[leg] += 1
+
+    def result(self):
+        L = self.seq_len
+        model = cpu_model()
+
+        def leg(name, cores, kind):
+            n, t = self.done[name], self.time[name]
+            return {"value": n * L / t, "unit": "tokens/s", "cores": cores, "kind": kind,
+                    "sample": "%d of the 128 requests, %d tokens each (1024 prompt + 127 decode forwards), one GDN "
+                              "layer, whole-sequence oracle passes (conv, bf16 rounding, gated delta rule) in fp64; "
+                              "%.1f s, half before and half after the GPU timed region" % (n, L, t),
+                    "cpu_model": model}
+        out = leg("serial", 1, "oracle")
+        out["multicore"] = leg("multi", self.cores, "oracle (the same source built with OpenMP: independent conv "
+                                                    "channels and (sequence, v-head) pairs on separate threads)")
+        return out
 
 
 def step_call_kinds(n_decodes, n_prefills, layers):
@@ -582,24 +705,56 @@ def main():
     kinds = [k for k in ("conv_varlen", "fused_decode", "recurrent_chunk", "chunk_and_decode")
              if any(k in ks for ks in plan_kinds)]
 
-    # ---- warm-up, then one instrumented pass (untimed) for the per-kernel shares
+    # ---- what one recorded event costs: each idles the stream for a few us
+    # on this GPU, and a bracketed run's span includes that idle time.  N
+    # fixed-length spin kernels timed as one run, then each inside its own
+    # event pair: the difference per pair is subtracted from every bracketed
+    # span below.
+    def event_cost_us(n=40, cycles=20000):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            torch.cuda._sleep(cycles)
+        e1.record(stream)
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a_, b_ in pairs:
+            a_.record(stream)
+            torch.cuda._sleep(cycles)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        whole = e0.elapsed_time(e1) / n
+        each = sum(a_.elapsed_time(b_) for a_, b_ in pairs) / n
+        return max(0.0, 1e3 * (each - whole))
+
+    # ---- warm-up, then one instrumented pass (untimed) per call kind for the
+    # per-kernel figures
     for _ in range(args.warmup):
         run_pass()
     torch.cuda.synchronize()
+    ev_cost = sorted(event_cost_us() for _ in range(5))[2]
     kern = {}
     for k in kinds:
         br, n_ev, wts, _ = bracket_runs(plan_kinds, k)
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
         run_pass((br, evs))
         torch.cuda.synchronize()
-        ms = span_ms(evs, wts)
+        raw = span_ms(evs, wts)
+        ms = raw - 1e-3 * ev_cost * sum(wts)
         n, nb, nf = totals(k)
         kern[k] = {"launches_per_step": n, "ms_per_step": ms, "avg_us": 1e3 * ms / max(n, 1),
+                   "avg_us_events_raw": 1e3 * raw / max(n, 1), "bracketed_runs": n_ev // 2,
                    "gb_per_s": nb / (ms * 1e-3) / 1e9 if ms else 0.0,
                    "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS if ms else 0.0}
         if nf:
             kern[k]["tflop_per_s"] = nf / (ms * 1e-3) / 1e12
     dominant = max(kinds, key=lambda k: kern[k]["ms_per_step"])
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # first half of the oracle's sample before the GPU's timed region
+        cpu = CpuBaseline(args.seed, trace.seq_len, args.cpu_sample_requests, args.cpu_multicore_requests)
+        cpu.half(0)
 
     # ---- timed region: the dominant kernel's runs bracketed by pre-created
     # events -- every long run, and every ROOFLINE_STRIDE-th one-launch run
@@ -615,11 +770,15 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    ms_dom = sum(span_ms(evs, wts) for evs in live) / args.steps
+    if cpu is not None:
+        cpu.half(1)
+
+    ms_dom = sum(span_ms(evs, wts) for evs in live) / args.steps - 1e-3 * ev_cost * sum(wts)
     n, nb, nf = totals(dominant)
     avg_us = 1e3 * ms_dom / n
     sample_note = ("events around every run of several consecutive launches and every %dth one-launch run "
-                   "(weighted): estimated total time of all %d launches per step" % (ROOFLINE_STRIDE, n))
+                   "(weighted): estimated total time of all %d launches per step, less the measured cost of "
+                   "each event pair (%.2f us)" % (ROOFLINE_STRIDE, n, ev_cost))
     if dominant == "recurrent_chunk":
         # matrix-core kernel (bf16 MFMA, fp32 operands split hi+lo); algorithmic
         # flops of the rule against the dense bf16 MFMA peak
@@ -641,7 +800,11 @@ def main():
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp32", "io_dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "fp32", "io_dtype": "bf16",
+        "dtype_detail": "bf16 activations and outputs (RNE); fp32 recurrent state and vector arithmetic "
+                        "(conv, decode); the chunkwise prefill's matrix products on bf16 MFMA with every fp32 "
+                        "operand split into hi + lo bf16 parts (16 significant bits) and fp32 accumulation",
+        "data": "synthetic",
         "config": {"workload": "c32 engine-step trace: 128 requests x (1024 prompt + 128 output tokens), "
                                "concurrency 32, 2048-token chunked-prefill budget, %d engine steps, "
                                "%d tokens per layer, %d GDN layers" % (len(steps), T_all, L),
@@ -650,11 +813,16 @@ def main():
                    "state_slots": SLOTS, "value_is": "tokens x layers / wall seconds"},
         "roofline": roof,
         "kernels": kern,
+        "event_pair_cost_us": ev_cost,
+        "context": PAGES_CONTEXT,
     }
     if not args.no_isolated:
         out["isolated"] = isolated(args.seed)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_sample_requests, trace.seq_len)
+        ceil = out["isolated"].get(dominant, {}).get("ceiling")
+        if ceil and roof["unit"] == "GB/s":
+            roof["ceiling"] = dict(ceil, frac_of_ceiling=roof["achieved"] / ceil["gb_per_s"])
+    if cpu is not None:
+        out["cpu_baseline"] = cpu.result()
     line = json.dumps(out)
     print(line, flush=True)
     if args.out:

@@ -4,7 +4,9 @@ Usage: python gated_deltanet_token_amd/build.py   (or __graft_entry__.build());
 this script never imports the package, which binds the library on import.
 
 Every .hip source under csrc/ is compiled to an object in _build/ and linked
-into gated_deltanet_token_amd/libgdn.so.  Packed-FP32 instruction selection
+into gated_deltanet_token_amd/libgdn.so; ceiling/ceiling.hip (the benchmark's
+reference copy kernels, not part of the library) into
+gated_deltanet_token_amd/ceiling/libgdn_ceiling.so.  Packed-FP32 instruction selection
 is disabled for all device code.
 """
 from __future__ import annotations
@@ -22,6 +24,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
+CEILING_SRC = os.path.join(PKG, "ceiling", "ceiling.hip")
+CEILING_LIB = os.path.join(PKG, "ceiling", "libgdn_ceiling.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -71,18 +75,25 @@ def hip_runtime_dir() -> str:
     return d
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with ThreadPoolExecutor(min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     rt = hip_runtime_dir()
     subprocess.check_call(["g++", "-shared", "-fPIC", "-o", tmp] + objs +
                           ["-L" + rt, "-lamdhip64", "-Wl,-rpath," + rt, "-Wl,--no-undefined"])
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    with ThreadPoolExecutor(min(8, len(srcs) + 1)) as ex:
+        objs = list(ex.map(_compile, srcs + [CEILING_SRC]))
+    _link(objs[:-1], LIB)
+    # the benchmark's reference copy / read-modify-write kernels, a library of
+    # their own (not part of libgdn)
+    _link(objs[-1:], CEILING_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", CEILING_LIB)
     return LIB
 
 
