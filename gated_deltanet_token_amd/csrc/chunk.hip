@@ -550,9 +550,10 @@ __device__ __forceinline__ void scan_rows_unit(const RecurrentArgs &a, const Chu
     // the start of the four phases of the chunk before: all at once they
     // filled the memory pipeline and held the wave at the issue for ~2,000
     // cycles.  Rows past the chunk end read its last token again (finite
-    // values, not zeroed): the prep gives a padded token beta = bgr = 0, a
-    // zero gate and a zero K^T column, so its R, U and U' are exactly zero
-    // and its Y rows, computed from the repeated token, are never used.
+    // values, not zeroed): the prep gives a padded token beta = bgr = 0 and a
+    // zero gate, so its R, U and U' are exactly zero, the K^T column it adds
+    // to the state update (the repeated token's k) multiplies zeros, and its
+    // Y rows, computed from the repeated token, are never used.
     auto fetch_kq = [&](St &st, int t0, int n) {
 #pragma unroll
         for (int j = 0; j < St::NK; ++j) {
