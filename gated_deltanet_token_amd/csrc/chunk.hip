@@ -199,6 +199,13 @@ __device__ __forceinline__ int chunks_before(const int32_t *qsl, int s, int num_
 // rows are not staged (the MFMA reads its q fragments from L2), and T reuses
 // the space of the k rows, which are dead once A and P are formed: 53 KB at
 // VPW = 2 (three workgroups per CU), 31 KB at VPW = 1 (five).
+//
+// A workgroup's work is one chain of dependent steps, and a 2,048-token
+// step has only about two workgroups per CU, so the order below keeps that
+// chain short: each wave issues the q loads of its first tile before
+// anything else, the waves with one tile fewer take the gates and the
+// per-token scalars, and every block of T goes to the workspace as soon as
+// it is final instead of in a pass at the end.
 template <int VPW>
 struct PrepSmem {
     union {
@@ -210,14 +217,56 @@ struct PrepSmem {
     float lam[VPW][CT], beta[VPW][CT];
 };
 
+// t-tile and i-tile of lower-triangular block b (b = bt (bt + 1) / 2 + bc)
+__device__ __forceinline__ void tile_of(int b, int &bt, int &bc) {
+    bt = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3;
+    bc = b - bt * (bt + 1) / 2;
+}
+
+// the q rows of t-tile bt as MFMA B operands, straight from L2 (zero past
+// the chunk end)
+__device__ __forceinline__ void load_qfrag(bf16x8 (&bq)[DKC / 32], const RecurrentArgs &a, int t0, int n, int hk,
+                                           int bt, int lr, int lq) {
+    const int t = 16 * bt + lr;
+    const __bf16 *qrow = reinterpret_cast<const __bf16 *>(a.q) + (int64_t)(t0 + min(t, n - 1)) * a.q_stride +
+                         hk * DKC + 8 * lq;
+#pragma unroll
+    for (int ks = 0; ks < DKC / 32; ++ks) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(qrow + 32 * ks);
+        bq[ks] = __builtin_bit_cast(bf16x8, t < n ? v : make_uint4(0, 0, 0, 0));
+    }
+}
+
+// block bi of T (final, in LDS) to the record as hi and lo bf16, by one
+// whole wave: lane l takes row l / 4, four consecutive columns.  The block
+// was written by this same wave's lanes in another layout; the fences keep
+// the compiler from moving the reads above those writes (a wave's LDS
+// accesses complete in order).
+__device__ __forceinline__ void store_tblock(const Blk &Tb, ChunkRec *rec, int bi, int lane) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int r = lane >> 2, c0 = 4 * (lane & 3);
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(&Tb[r][c0]);
+    bf16x4 h, l;
+    split4(v, h, l);
+    st4(&rec->TP[0][bi][r][c0], h);
+    st4(&rec->TP[1][bi][r][c0], l);
+}
+
 template <int VPW>
 __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, ChunkRec *recs) {
     constexpr int NT = NTH * VPW, NW = NT / 64;
+    constexpr int GW = NW - VPW;                // waves GW + v: gates and per-token scalars of v-head v
     __shared__ PrepSmem<VPW> sm;
     const int HV = a.num_v_heads, NP = HV / VPW;
+    // head-pair-major, XCD-contiguous: an XCD prepares all chunks of a range
+    // of v-heads, the heads whose scan workgroups it also runs, so the scan
+    // finds the records in its own L2
     const int work = xcd_contiguous(blockIdx.x, gridDim.x);
-    const int h0 = (work % NP) * VPW;           // the workgroup's first v-head
-    const int gch = work / NP;                  // global chunk index
+    const int mcg = gridDim.x / NP;             // chunks the grid covers (an upper bound)
+    const int h0 = (work / mcg) * VPW;          // the workgroup's first v-head
+    const int gch = work % mcg;                 // global chunk index
     int s, j, lo, hi;                           // (sequence, chunk within it, its tokens)
     locate_chunk(a.qsl, a.num_seqs, a.num_tokens, gch, s, j, lo, hi);
     // (a padded sequence, state index < 0, is prepared too: its records are
@@ -231,8 +280,16 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lr = lane & 15, lq = lane >> 4;
 
+    // q of the wave's first tile (b = w), in flight during stage 0
+    bf16x8 bq[DKC / 32];
+    {
+        int bt, bc;
+        tile_of(w, bt, bc);
+        load_qfrag(bq, a, t0, n, hk, bt, lr, lq);
+    }
+
     // ---- stage 0: k/q rows and norms (first four waves); cumulative decay of
-    // v-head v (wave v)
+    // v-head v (wave GW + v)
     if (tid < NTH) {
         const int tok = tid >> 2, part = tid & 3;
         uint4 kv[4], qv[4];
@@ -269,30 +326,30 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
             sm.rk[tok] = a.l2norm ? rsqrtf(skk + 1e-6f) : 1.f;
             sm.rq[tok] = a.l2norm ? rsqrtf(sqq + 1e-6f) : 1.f;
         }
-        if (w < VPW) {
-            // padded tokens: g = 0 and beta = 0 make them exact no-ops
-            const int h = h0 + w;
-            float gg = lane < n ? a.g[(int64_t)(t0 + lane) * HV + h] : 0.f;
-            const float bb = lane < n ? a.beta[(int64_t)(t0 + lane) * HV + h] : 0.f;
+    }
+    if (w >= GW) {
+        // padded tokens: g = 0 and beta = 0 make them exact no-ops
+        const int v = w - GW, h = h0 + v;
+        float gg = lane < n ? a.g[(int64_t)(t0 + lane) * HV + h] : 0.f;
+        const float bb = lane < n ? a.beta[(int64_t)(t0 + lane) * HV + h] : 0.f;
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float up = __shfl_up(gg, off, 64);
-                if (lane >= off) gg += up;
-            }
-            sm.lam[w][lane] = gg;
-            sm.beta[w][lane] = bb;
+        for (int off = 1; off < 64; off <<= 1) {
+            const float up = __shfl_up(gg, off, 64);
+            if (lane >= off) gg += up;
         }
+        sm.lam[v][lane] = gg;
+        sm.beta[v][lane] = bb;
     }
     __syncthreads();
 
-    // per-token scalars for the scan (wave v for v-head v)
-    if (w < VPW) {
-        const int t = lane;
-        ChunkRec *rec = recs + (int64_t)gch * HV + h0 + w;
-        const float lam = sm.lam[w][t], lamC = sm.lam[w][CT - 1];
+    // per-token scalars for the scan (wave GW + v for v-head v)
+    if (w >= GW) {
+        const int v = w - GW, t = lane;
+        ChunkRec *rec = recs + (int64_t)gch * HV + h0 + v;
+        const float lam = sm.lam[v][t], lamC = sm.lam[v][CT - 1];
         const float G = expf(lam), rk = sm.rk[t];
-        rec->beta[t] = sm.beta[w][t];
-        rec->bgr[t] = sm.beta[w][t] * G * rk;
+        rec->beta[t] = sm.beta[v][t];
+        rec->bgr[t] = sm.beta[v][t] * G * rk;
         rec->sqg[t] = a.scale * sm.rq[t] * G;
         rec->u2f[t] = expf(lamC - lam) * rk;
         rec->gC[t] = expf(lamC);
@@ -300,21 +357,12 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
     // ---- stage 1: the ten lower-triangular tiles (t-tile bt, i-tile bc) of
     // K K^T and K Q^T, round-robin over the waves, laid out so each lane holds
     // 4 consecutive i of one row t; per v-head, A (fp32) into its LDS block and
-    // P (hi/lo) to the workspace with 8-byte stores
+    // P (hi/lo) to the workspace with 8-byte stores.  The next tile's q loads
+    // go out as soon as this tile's products have read its q.
     for (int b = w; b < NBLK16; b += NW) {
-        const int bt = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3, bc = b - bt * (bt + 1) / 2;
+        int bt, bc;
+        tile_of(b, bt, bc);
         const int t = 16 * bt + lr, i0 = 16 * bc + 4 * lq;
-        // q rows of t-tile bt as B operands, straight from L2 (zero past the chunk end)
-        bf16x8 bq[DKC / 32];
-        {
-            const __bf16 *qrow = reinterpret_cast<const __bf16 *>(a.q) + (int64_t)(t0 + min(t, n - 1)) * a.q_stride +
-                                 hk * DKC + 8 * lq;
-#pragma unroll
-            for (int ks = 0; ks < DKC / 32; ++ks) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(qrow + 32 * ks);
-                bq[ks] = __builtin_bit_cast(bf16x8, t < n ? v : make_uint4(0, 0, 0, 0));
-            }
-        }
         f32x4 kk = {0.f, 0.f, 0.f, 0.f}, kq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < DKC / 32; ++ks) {
@@ -322,6 +370,11 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
             const bf16x8 bk = frag(&sm.u.K[0][0], LDK, 16 * bt, 32 * ks, lane);
             kk = mma(ai, bk, kk);
             kq = mma(ai, bq[ks], kq);
+        }
+        if (b + NW < NBLK16) {
+            int nbt, nbc;
+            tile_of(b + NW, nbt, nbc);
+            load_qfrag(bq, a, t0, n, hk, nbt, lr, lq);
         }
         const float rk_t = sm.rk[t], rq_t = sm.rq[t];
 #pragma unroll
@@ -349,6 +402,7 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
     // by block (T overwrites the k rows)
     {
         const int v = w >> 2, wb = w & 3;
+        ChunkRec *rec = recs + (int64_t)gch * HV + h0 + v;
         if (lane < 16) {
             // diagonal block wb by forward substitution; lane j owns column j
             const Blk &Ad = sm.A[v][blk(wb, wb)];
@@ -365,9 +419,10 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
             for (int r = 0; r < 16; ++r) Td[r][lane] = xcol[r];
         }
         __syncthreads();
+        store_tblock(sm.u.T[v][blk(wb, wb)], rec, blk(wb, wb), lane);
         // T_bc = -T_bb (sum_{c<=m<b} A_bm T_mc); wave c of the v-head walks
         // down column block c, so every input is its own earlier result or a
-        // diagonal block
+        // diagonal block; each block is stored once final
         const int c = wb;
         for (int b = c + 1; b < 4 && c < 3; ++b) {
             f32x4 m = {0.f, 0.f, 0.f, 0.f};
@@ -376,28 +431,7 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
             f32x4 t = {0.f, 0.f, 0.f, 0.f};
             t = mm16(sm.u.T[v][blk(b, b)], sm.u.T[v][blk(b, c)], t, lane);
             put16(sm.u.T[v][blk(b, c)], t, -1.f, lane);
-        }
-        __syncthreads();
-        // hi/lo to the workspace, the ten blocks of each v-head only, 8
-        // consecutive entries per lane
-#pragma unroll
-        for (int e = 0; e < (VPW * NBLK16 * 32 + NT - 1) / NT; ++e) {
-            const int idx = tid + NT * e;           // 320 groups of 8 per v-head
-            if (idx < VPW * NBLK16 * 32) {
-                const int vv = idx / (NBLK16 * 32), q = idx - vv * (NBLK16 * 32);
-                const int b = q >> 5, r = (q >> 1) & 15, c0 = (q & 1) * 8;
-                bf16x8 hv, lv;
-#pragma unroll
-                for (int qq = 0; qq < 8; ++qq) {
-                    __bf16 hi, lo;
-                    split(sm.u.T[vv][b][r][c0 + qq], hi, lo);
-                    hv[qq] = hi;
-                    lv[qq] = lo;
-                }
-                ChunkRec *rec = recs + (int64_t)gch * HV + h0 + vv;
-                st8(&rec->TP[0][b][r][c0], hv);
-                st8(&rec->TP[1][b][r][c0], lv);
-            }
+            store_tblock(sm.u.T[v][blk(b, c)], rec, blk(b, c), lane);
         }
     }
 }
@@ -504,8 +538,9 @@ struct RowStage {
 };
 
 // One scan workgroup's work: the 16 NW v rows from 16 NW vb of one
-// (sequence s, v-head h), work = (s HV + h) n_vblocks + vb, through that
-// sequence's chunks.  Called by all 64 NW threads of a workgroup; sm is the
+// (sequence s, v-head h), work = (h num_seqs + s) n_vblocks + vb, through that
+// sequence's chunks (head-major, like the prep's order, so an XCD scans the
+// v-heads whose records it prepared).  Called by all 64 NW threads of a workgroup; sm is the
 // workgroup's LDS.  Each kernel inlines its own instance (TAG): with one
 // instance shared by two kernels, hipcc 7.2 scheduled the scan kernel's loop
 // with 26 more AGPR moves.
@@ -517,8 +552,8 @@ __device__ __forceinline__ void scan_rows_unit(const RecurrentArgs &a, const Chu
     const int HV = a.num_v_heads;
     const int vb = work % n_vblocks;
     const int sh = work / n_vblocks;
-    const int h = sh % HV;
-    const int s = sh / HV;
+    const int s = sh % a.num_seqs;
+    const int h = sh / a.num_seqs;
     const int slot = a.state_indices[s];
     if ((unsigned)slot >= (unsigned)a.num_slots) return;   // padding, or outside the pool
     int t_begin, t_end;
