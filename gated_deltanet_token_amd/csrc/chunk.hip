@@ -79,14 +79,8 @@ __device__ __forceinline__ f32x4 mma(const bf16x8 &a, const bf16x8 &b, const f32
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void split(float v, __bf16 &hi, __bf16 &lo) {
-    hi = (__bf16)v;
-    lo = (__bf16)(v - (float)hi);
-}
-
-// four fp32 -> hi and lo bf16x4 (8-byte stores).  The same values as split()
-// (hi = RNE(v), lo = RNE(v - hi)), converted two at a time with the packed
-// conversion.
+// four fp32 -> hi and lo bf16x4 (8-byte stores): hi = RNE(v), lo =
+// RNE(v - hi), converted two at a time with the packed conversion.
 __device__ __forceinline__ void split4(const f32x4 &v, bf16x4 &hi, bf16x4 &lo) {
     typedef float f32x2v __attribute__((ext_vector_type(2)));
     typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
@@ -98,11 +92,21 @@ __device__ __forceinline__ void split4(const f32x4 &v, bf16x4 &hi, bf16x4 &lo) {
     lo = __builtin_shufflevector(l01, l23, 0, 1, 2, 3);
 }
 
-// Workspace stores are plain: the scan reads the records right after the
-// prep, and finds them in the caches (streaming stores for the records made
-// the whole call 2-3% slower).  The scan's final state is streaming.
-__device__ __forceinline__ void st4(__bf16 *p, const bf16x4 &v) { *reinterpret_cast<bf16x4 *>(p) = v; }
-__device__ __forceinline__ void st8(__bf16 *p, const bf16x8 &v) { *reinterpret_cast<bf16x8 *>(p) = v; }
+// Workspace stores are written through the L2 (sc1): the scan reads the
+// records right after the prep, on the same XCD (both kernels order their
+// work head-major), and finds them in its L2, while the end of the prep has
+// no dirty lines to write back.  A relaxed device-scope atomic store is how
+// HIP expresses such a store; it is an ordinary 8- or 4-byte vector store
+// with the sc1 bit.  (Streaming stores for the records made the whole call
+// 2-3% slower; plain ones left the prep's end writing back its records.)
+// The scan's final state is streaming.
+__device__ __forceinline__ void st4(__bf16 *p, const bf16x4 &v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_f32(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // A 64 x 64 lower-triangular fp32 matrix in LDS as its ten 16 x 16 blocks
 // (b, c), b >= c, block index b (b + 1) / 2 + c; rows padded to 20 floats
@@ -348,11 +352,11 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
         ChunkRec *rec = recs + (int64_t)gch * HV + h0 + v;
         const float lam = sm.lam[v][t], lamC = sm.lam[v][CT - 1];
         const float G = expf(lam), rk = sm.rk[t];
-        rec->beta[t] = sm.beta[v][t];
-        rec->bgr[t] = sm.beta[v][t] * G * rk;
-        rec->sqg[t] = a.scale * sm.rq[t] * G;
-        rec->u2f[t] = expf(lamC - lam) * rk;
-        rec->gC[t] = expf(lamC);
+        st_f32(&rec->beta[t], sm.beta[v][t]);
+        st_f32(&rec->bgr[t], sm.beta[v][t] * G * rk);
+        st_f32(&rec->sqg[t], a.scale * sm.rq[t] * G);
+        st_f32(&rec->u2f[t], expf(lamC - lam) * rk);
+        st_f32(&rec->gC[t], expf(lamC));
     }
     // ---- stage 1: the ten lower-triangular tiles (t-tile bt, i-tile bc) of
     // K K^T and K Q^T, round-robin over the waves, laid out so each lane holds

@@ -23,7 +23,7 @@ constexpr int kConvThreads = 256;                       // 4 waves
 constexpr int kConvTile = kConvThreads * kConvVec;      // 2048 channels
 constexpr int kChunk = 8;                               // tokens per descriptor
 
-template <int THREADS, bool SILU>
+template <int THREADS, bool SILU, bool WT>
 __global__ __launch_bounds__(THREADS) void conv_varlen_kernel(
     const uint16_t *__restrict__ x, int64_t x_stride, const uint16_t *__restrict__ weight,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ conv_state,
@@ -86,8 +86,12 @@ __global__ __launch_bounds__(THREADS) void conv_varlen_kernel(
 #pragma unroll
     for (int i = 0; i < 3; ++i) h[i] = make_uint4(h[i].x & keep, h[i].y & keep, h[i].z & keep, h[i].w & keep);
 
-    // Output rows, on plain stores: the prefill path reads them right away
-    // (the chunkwise rule's q, k and v), and finds them in the caches.
+    // Output rows, written through the L2 (WT: a buffer resource over the
+    // chunk's rows, whose range also drops the rows past the chunk end): the
+    // prefill path reads them right away (the chunkwise rule's q, k and v)
+    // and finds them in the caches, and the end of the kernel has no dirty
+    // lines to write back.  (Plain stores when the row stride is too large
+    // for 32-bit buffer offsets.)
     // Window row j is h[j] for j < 3, else r[j - 3]; pair j holds window
     // rows (j, j + 1) and serves output rows j and j - 2.
     RowPairs pr[kChunk + 2];
@@ -97,10 +101,17 @@ __global__ __launch_bounds__(THREADS) void conv_varlen_kernel(
         const uint4 &newer = j + 1 < 3 ? h[j + 1] : r[j - 2];
         pr[j] = row_pairs(older, newer);
     }
+    const __amdgpu_buffer_rsrc_t y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        y + (int64_t)t0 * y_stride, (short)0, WT ? n * (int)y_stride * 2 : 0, kBufferFlags);
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
         const uint4 out = conv_pairs(taps, pr[i], pr[i + 2], SILU);
-        if (i < n) *reinterpret_cast<uint4 *>(y + (int64_t)(t0 + i) * y_stride + c0) = out;
+        if (WT) {
+            const u32x4 o4 = {out.x, out.y, out.z, out.w};
+            __builtin_amdgcn_raw_buffer_store_b128(o4, y_rsrc, (i * (int)y_stride + c0) * 2, 0, kBufferWriteThrough);
+        } else if (i < n) {
+            *reinterpret_cast<uint4 *>(y + (int64_t)(t0 + i) * y_stride + c0) = out;
+        }
     }
 
     if (first) {
@@ -151,16 +162,20 @@ hipError_t launch_conv_varlen_t(const ConvVarlenArgs &a, hipStream_t stream) {
     const long long blocks = (long long)a.n_chunks * n_tiles;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (a.silu)
-        hipLaunchKernelGGL((conv_varlen_kernel<THREADS, true>), dim3((unsigned)blocks), dim3(THREADS), 0, stream,
-                           a.x, a.x_stride, a.weight, a.bias, a.conv_state, a.qsl, a.state_indices, a.has_init,
-                           a.chunks, a.y, a.y_stride, a.channels, n_tiles, a.num_seqs, a.num_slots,
-                           a.num_tokens);
-    else
-        hipLaunchKernelGGL((conv_varlen_kernel<THREADS, false>), dim3((unsigned)blocks), dim3(THREADS), 0, stream,
-                           a.x, a.x_stride, a.weight, a.bias, a.conv_state, a.qsl, a.state_indices, a.has_init,
-                           a.chunks, a.y, a.y_stride, a.channels, n_tiles, a.num_seqs, a.num_slots,
-                           a.num_tokens);
+    // the write-through path addresses the chunk's 8 rows with 32-bit byte offsets
+    const bool wt = a.y_stride <= ((int64_t)1 << 26);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(THREADS), 0, stream, a.x, a.x_stride, a.weight,
+                           a.bias, a.conv_state, a.qsl, a.state_indices, a.has_init, a.chunks, a.y, a.y_stride,
+                           a.channels, n_tiles, a.num_seqs, a.num_slots, a.num_tokens);
+    };
+    if (a.silu) {
+        if (wt) go(conv_varlen_kernel<THREADS, true, true>);
+        else go(conv_varlen_kernel<THREADS, true, false>);
+    } else {
+        if (wt) go(conv_varlen_kernel<THREADS, false, true>);
+        else go(conv_varlen_kernel<THREADS, false, false>);
+    }
     return hipGetLastError();
 }
 

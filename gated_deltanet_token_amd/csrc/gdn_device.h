@@ -117,6 +117,10 @@ constexpr int kNumXcd = 8;
 constexpr int kBufferFlags = 0x00020000;
 // cache-policy operand of the buffer builtins for a streaming (nt) access
 constexpr int kBufferStream = 2;
+// cache-policy operand for a store written through the L2 (sc1, device
+// scope): the line stays in the writing XCD's L2 for a reader there, and is
+// not left dirty for the end of the kernel to write back
+constexpr int kBufferWriteThrough = 16;
 
 __device__ __forceinline__ int xcd_contiguous(int bid, int n) {
     const int xcd = bid % kNumXcd;
