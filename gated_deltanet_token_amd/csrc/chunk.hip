@@ -813,8 +813,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_scan_rows_kernel(RecurrentAr
 // where the decode kernel fits two.
 constexpr int kMixedThreads = 256;
 static_assert(kFusedThreads == kMixedThreads, "decode units and 64-row scan workgroups are both 4 waves");
-static_assert(sizeof(RowScanSmem<4>) >= kMaxGroupChannels * sizeof(uint16_t),
-              "a decode unit's conv output fits in the scan's LDS");
+static_assert(sizeof(RowScanSmem<4>) >= fused_unit_lds_bytes(0, kMaxGroupChannels / 8, 8),
+              "a decode unit's conv output, decays and betas fit in the scan's LDS");
 
 __global__ __launch_bounds__(kMixedThreads, 1) void chunk_scan_decode_kernel(RecurrentArgs a, const ChunkRec *recs,
                                                                            int n_vblocks,
@@ -826,8 +826,12 @@ __global__ __launch_bounds__(kMixedThreads, 1) void chunk_scan_decode_kernel(Rec
         if (bid < n_scan) scan_rows_unit<4, 1>(a, recs, n_vblocks, xcd_contiguous(bid, n_scan), sm);
     } else {
         // n_scan_pad is a multiple of the XCD count: bid - n_scan_pad stays on bid's XCD
-        fused_decode_unit<DKC, kFusedRows>(f, xcd_contiguous(bid - n_scan_pad, n_dec),
-                                           reinterpret_cast<uint16_t *>(&sm));
+        // a unit runs alone on its CU here: the latency form when the group is one full pass
+        const int unit = xcd_contiguous(bid - n_scan_pad, n_dec);
+        if (fused_unit_full<DKC>(f.num_v_heads / f.num_k_heads * f.dv))
+            fused_decode_unit<DKC, kFusedRows, true>(f, unit, reinterpret_cast<uint16_t *>(&sm));
+        else
+            fused_decode_unit<DKC, kFusedRows, false>(f, unit, reinterpret_cast<uint16_t *>(&sm));
     }
 }
 

@@ -27,10 +27,41 @@ constexpr int kFusedThreads = 256;
 constexpr int kFusedRows = 8;                      // rows per lane group per pass
 constexpr int kMaxGroupChannels = 8192;            // q + k + v channels of one head group
 
-// bid: the unit, b * num_k_heads + hk.  act: LDS for the conv output of the
-// group, (2 DK + (HV / HK) dv) bf16.  Called by all kFusedThreads threads of
-// a workgroup.
-template <int DK, int R>
+// LDS of a unit: the conv output of the group, (2 DK + (HV / HK) dv) bf16,
+// then -- in the form that runs alone on its CU -- the decay and beta of each
+// of its HV / HK v heads as fp32 (after rounding the bf16 count up to even)
+__host__ __device__ constexpr int fused_unit_lds_bytes(int dk, int grp, int dv) {
+    return ((2 * dk + grp * dv + 1) & ~1) * 2 + 2 * grp * 4;
+}
+
+// whether a group of n_rows state rows is exactly one pass of a unit
+template <int DK>
+__host__ __device__ constexpr bool fused_unit_full(int n_rows) {
+    return n_rows == kFusedRows * (kFusedThreads / RowLayout<DK>::G);
+}
+
+// bid: the unit, b * num_k_heads + hk.  act: LDS of at least
+// fused_unit_lds_bytes.  Called by all kFusedThreads threads of a workgroup.
+//
+// Two forms with the same arithmetic (bit-identical results):
+//  * ALONE = false, for the decode kernel, where every CU holds two units
+//    and the launch is bound by HBM bandwidth: the first pass of state
+//    loads goes out right after the conv loads, and each row reads its v
+//    head's decay and beta when it needs them.  (The conv arithmetic then
+//    waits for the state loads too: they are conditional, and the compiler
+//    waits for every outstanding load at the join.  Letting the conv go
+//    ahead, so that rows are processed and stored as their loads arrive,
+//    made the decode kernel 4-7% slower: the stores then mix with the
+//    loads of the other units.)
+//  * ALONE = true, for the mixed-step grid, where a unit runs alone on a CU
+//    next to the scan and its latency is what counts; only for FULL groups
+//    (fused_unit_full).  Load order: the decay and beta of the thread's v
+//    head, its conv vector's window, input and taps, then the state rows --
+//    all unconditional, so the conv waits only for its own loads (memory
+//    loads complete in order) -- and the decays and betas reach the rows
+//    through LDS, so no row waits for a global load of its own.  Against
+//    the first form, the c32 mixed step's recurrence measured 68.4 -> 63.5 us.
+template <int DK, int R, bool ALONE = false>
 __device__ __forceinline__ void fused_decode_unit(const FusedDecodeArgs &a, int bid, uint16_t *act) {
     using L = RowLayout<DK>;
     constexpr int G = L::G, E = L::E, M = L::M;
@@ -50,7 +81,8 @@ __device__ __forceinline__ void fused_decode_unit(const FusedDecodeArgs &a, int 
     const int n_rows = nv;
 
     // one pass of state rows: row r of this lane group, loaded as streaming
-    // 16-byte vectors (each state element is read and written once)
+    // 16-byte vectors (each state element is read and written once); rows
+    // past the group are not loaded and start at zero
     int row[R];
     bool valid[R];
     float S[R][E];
@@ -58,7 +90,7 @@ __device__ __forceinline__ void fused_decode_unit(const FusedDecodeArgs &a, int 
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             row[r] = base + r * ROWS_PER_PASS + tid / G;      // row within the group
-            valid[r] = row[r] < n_rows;
+            valid[r] = ALONE || row[r] < n_rows;
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -76,11 +108,13 @@ __device__ __forceinline__ void fused_decode_unit(const FusedDecodeArgs &a, int 
         }
     };
 
-    // ---- conv update of the group's channels.  The first pass of state
-    // loads is issued right after the conv loads: it does not depend on the
-    // conv, so its latency overlaps the conv arithmetic and the barrier.
-    for (int c = tid; c < n_vec; c += kFusedThreads) {
-        const int lc = c * kConvVec;                          // channel within the group (q | k | v)
+    // ---- conv update of the group's channels, one 8-channel vector per
+    // thread and iteration.  The first pass of state loads is issued right
+    // after the first vector's loads: it does not depend on the conv, so its
+    // latency overlaps the conv arithmetic and the barrier.
+    // (ALONE: one vector of the conv, from a clamped, always-valid channel)
+    auto conv_vec = [&](int c, bool load_state) {
+        const int lc = min(c, n_vec - 1) * kConvVec;          // channel within the group (q | k | v)
         int ch;                                               // channel within the conv row
         if (lc < nq) ch = hk * DK + lc;
         else if (lc < 2 * nq) ch = HK * DK + hk * DK + (lc - nq);
@@ -92,15 +126,63 @@ __device__ __forceinline__ void fused_decode_unit(const FusedDecodeArgs &a, int 
         const uint4 xv = *reinterpret_cast<const uint4 *>(a.x + (int64_t)b * a.x_stride + ch);
         ConvTaps taps;
         load_taps(taps, a.conv_weight, a.conv_bias, ch);
-        if (c == tid) load_rows(0);
-        const uint4 out = conv_row(taps, s0, s1, s2, xv, a.silu != 0);
-        *reinterpret_cast<uint4 *>(st) = s1;
-        *reinterpret_cast<uint4 *>(st + a.channels) = s2;
-        *reinterpret_cast<uint4 *>(st + 2 * (int64_t)a.channels) = xv;
-        if (a.y) *reinterpret_cast<uint4 *>(a.y + (int64_t)b * a.y_stride + ch) = out;
-        *reinterpret_cast<uint4 *>(&act[lc]) = out;
+        if (load_state) {
+            // keep the compiler from moving the conv loads below the state
+            // loads, or into the branch below
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            load_rows(0);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (c < n_vec) {
+            const uint4 out = conv_row(taps, s0, s1, s2, xv, a.silu != 0);
+            *reinterpret_cast<uint4 *>(st) = s1;
+            *reinterpret_cast<uint4 *>(st + a.channels) = s2;
+            *reinterpret_cast<uint4 *>(st + 2 * (int64_t)a.channels) = xv;
+            if (a.y) *reinterpret_cast<uint4 *>(a.y + (int64_t)b * a.y_stride + ch) = out;
+            *reinterpret_cast<uint4 *>(&act[lc]) = out;
+        }
+    };
+    // ALONE: decay and beta of v head min(tid, grp - 1) of the group; threads
+    // t < grp publish theirs through LDS
+    float *gates = reinterpret_cast<float *>(act + ((2 * nq + nv + 1) & ~1));
+    if constexpr (ALONE) {
+        const int gh = hk * grp + min(tid, grp - 1);
+        const float g_own = a.g[(int64_t)b * HV + gh];
+        const float b_own = a.beta[(int64_t)b * HV + gh];
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        conv_vec(tid, true);
+        for (int c = tid + kFusedThreads; c < n_vec; c += kFusedThreads) conv_vec(c, false);
+        if (tid < grp) {
+            gates[tid] = expf(g_own);
+            gates[grp + tid] = b_own;
+        }
+    } else {
+        for (int c = tid; c < n_vec; c += kFusedThreads) {
+            const int lc = c * kConvVec;                      // channel within the group (q | k | v)
+            int ch;                                           // channel within the conv row
+            if (lc < nq) ch = hk * DK + lc;
+            else if (lc < 2 * nq) ch = HK * DK + hk * DK + (lc - nq);
+            else ch = 2 * HK * DK + hk * nv + (lc - 2 * nq);
+            uint16_t *st = a.conv_state + (int64_t)slot * 3 * a.channels + ch;
+            const uint4 s0 = *reinterpret_cast<const uint4 *>(st);
+            const uint4 s1 = *reinterpret_cast<const uint4 *>(st + a.channels);
+            const uint4 s2 = *reinterpret_cast<const uint4 *>(st + 2 * (int64_t)a.channels);
+            const uint4 xv = *reinterpret_cast<const uint4 *>(a.x + (int64_t)b * a.x_stride + ch);
+            ConvTaps taps;
+            load_taps(taps, a.conv_weight, a.conv_bias, ch);
+            if (c == tid) load_rows(0);
+            const uint4 out = conv_row(taps, s0, s1, s2, xv, a.silu != 0);
+            *reinterpret_cast<uint4 *>(st) = s1;
+            *reinterpret_cast<uint4 *>(st + a.channels) = s2;
+            *reinterpret_cast<uint4 *>(st + 2 * (int64_t)a.channels) = xv;
+            if (a.y) *reinterpret_cast<uint4 *>(a.y + (int64_t)b * a.y_stride + ch) = out;
+            *reinterpret_cast<uint4 *>(&act[lc]) = out;
+        }
+        if (tid >= n_vec) load_rows(0);
     }
-    if (tid >= n_vec) load_rows(0);
     __syncthreads();
 
     // ---- gated delta rule, one token, for the grp * dv rows of the group
@@ -114,14 +196,14 @@ __device__ __forceinline__ void fused_decode_unit(const FusedDecodeArgs &a, int 
         }
     const TokenFactors f = token_factors<G, E>(kf, qf, a.l2norm != 0);
 
-    for (int base = 0; base < n_rows; base += R * ROWS_PER_PASS) {
+    for (int base = 0; base < (ALONE ? 1 : n_rows); base += R * ROWS_PER_PASS) {
         if (base > 0) load_rows(base);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int rr = min(row[r], n_rows - 1);
             const int h = hk * grp + rr / dv, i = rr % dv;
-            const float alpha = expf(a.g[(int64_t)b * HV + h]);
-            const float beta = a.beta[(int64_t)b * HV + h];
+            const float alpha = ALONE ? gates[rr / dv] : expf(a.g[(int64_t)b * HV + h]);
+            const float beta = ALONE ? gates[grp + rr / dv] : a.beta[(int64_t)b * HV + h];
             const float v = bf16_to_f32(act[2 * nq + rr]);
             const float out = row_step<G, E>(S[r], kf, qf, f, alpha, beta, v, a.scale);
             if (valid[r]) {
