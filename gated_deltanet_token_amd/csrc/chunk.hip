@@ -79,6 +79,13 @@ __device__ __forceinline__ f32x4 mma(const bf16x8 &a, const bf16x8 &b, const f32
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
+// exp(x) as one hardware 2^x (v_exp_f32, about 1 ulp) of x log2(e): the
+// rounding of the product adds a relative error of about |x| 2^-24 (below
+// 1e-5 for every |x| < 100; beyond that the decay is below 1e-43 and flushes
+// to zero).  The decays within a chunk use it; the library expf takes some
+// ten instructions more per call.
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
 // four fp32 -> hi and lo bf16x4 (8-byte stores): hi = RNE(v), lo =
 // RNE(v - hi), converted two at a time with the packed conversion.
 __device__ __forceinline__ void split4(const f32x4 &v, bf16x4 &hi, bf16x4 &lo) {
@@ -388,7 +395,7 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = i0 + e;
-                const float decay = i <= t ? expf(lam_t - sm.lam[v][i]) : 0.f;
+                const float decay = i <= t ? exp_fast(lam_t - sm.lam[v][i]) : 0.f;
                 av[e] = i < t ? beta_t * rk_t * sm.rk[i] * decay * kk[e] : 0.f;
                 pv[e] = i <= t ? a.scale * rq_t * sm.rk[i] * decay * kq[e] : 0.f;
             }
@@ -408,34 +415,61 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
         const int v = w >> 2, wb = w & 3;
         ChunkRec *rec = recs + (int64_t)gch * HV + h0 + v;
         if (lane < 16) {
-            // diagonal block wb by forward substitution; lane j owns column j
+            // diagonal block wb by forward substitution, lane j owning column
+            // j, swept by columns: once x_i is final, every later row takes
+            // its term at once (the same sums in the same order as row by
+            // row, with independent multiply-adds in each step)
             const Blk &Ad = sm.A[v][blk(wb, wb)];
-            float xcol[16];
+            float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = r == lane ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) x[r] = r == lane ? 1.f : 0.f;
 #pragma unroll
-                for (int i = 0; i < r; ++i) acc = __builtin_fmaf(-Ad[r][i], xcol[i], acc);
-                xcol[r] = acc;
-            }
+            for (int i = 0; i < 15; ++i)
+#pragma unroll
+                for (int r = i + 1; r < 16; ++r) x[r] = __builtin_fmaf(-Ad[r][i], x[i], x[r]);
             Blk &Td = sm.u.T[v][blk(wb, wb)];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Td[r][lane] = xcol[r];
+            for (int r = 0; r < 16; ++r) Td[r][lane] = x[r];
         }
         __syncthreads();
         store_tblock(sm.u.T[v][blk(wb, wb)], rec, blk(wb, wb), lane);
-        // T_bc = -T_bb (sum_{c<=m<b} A_bm T_mc); wave c of the v-head walks
-        // down column block c, so every input is its own earlier result or a
-        // diagonal block; each block is stored once final
-        const int c = wb;
-        for (int b = c + 1; b < 4 && c < 3; ++b) {
+        // The off-diagonal blocks as 2 x 2 block inverses of the 32 x 32
+        // halves T1 = (T00, T10, T11) and T2 = (T22, T32, T33), then the
+        // lower-left half -T2 A21 T1 (A21 = A20, A21, A30, A31):
+        //   level 1: T10 = -T11 A10 T00 (wave 0), T32 = -T33 A32 T22 (wave 1)
+        //   level 2: X = A21 T1, one block per wave, written over A21
+        //   level 3: T20 = -T22 X20, T21 = -T22 X21, T30 = -(T32 X20 + T33 X30),
+        //            T31 = -(T32 X21 + T33 X31), one block per wave
+        // Every product is a 16 x 16 fp32 block product on the matrix cores;
+        // the longest chain is six of them.
+        if (wb < 2) {
+            const int b = wb == 0 ? 1 : 3, c = b - 1;       // T10 or T32
             f32x4 m = {0.f, 0.f, 0.f, 0.f};
-            for (int mm = c; mm < b; ++mm) m = mm16(sm.A[v][blk(b, mm)], sm.u.T[v][blk(mm, c)], m, lane);
+            m = mm16(sm.A[v][blk(b, c)], sm.u.T[v][blk(c, c)], m, lane);
             put16(sm.u.T[v][blk(b, c)], m, 1.f, lane);
             f32x4 t = {0.f, 0.f, 0.f, 0.f};
             t = mm16(sm.u.T[v][blk(b, b)], sm.u.T[v][blk(b, c)], t, lane);
             put16(sm.u.T[v][blk(b, c)], t, -1.f, lane);
             store_tblock(sm.u.T[v][blk(b, c)], rec, blk(b, c), lane);
+        }
+        __syncthreads();
+        const int xb = 2 + (wb >> 1), xc = wb & 1;          // this wave's block (xb, xc) of the lower-left half
+        {
+            // X_bc = A_b0 T_0c + A_b1 T_1c (T_01 = 0)
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (xc == 0) x = mm16(sm.A[v][blk(xb, 0)], sm.u.T[v][blk(0, 0)], x, lane);
+            x = mm16(sm.A[v][blk(xb, 1)], sm.u.T[v][blk(1, xc)], x, lane);
+            __syncthreads();                                 // every A_b0, A_b1 read before any is overwritten
+            put16(sm.A[v][blk(xb, xc)], x, 1.f, lane);
+        }
+        __syncthreads();
+        {
+            // T_bc = -(T_b2 X_2c + T_b3 X_3c) (T_23 = 0)
+            f32x4 t = {0.f, 0.f, 0.f, 0.f};
+            t = mm16(sm.u.T[v][blk(xb, 2)], sm.A[v][blk(2, xc)], t, lane);
+            if (xb == 3) t = mm16(sm.u.T[v][blk(3, 3)], sm.A[v][blk(3, xc)], t, lane);
+            put16(sm.u.T[v][blk(xb, xc)], t, -1.f, lane);
+            store_tblock(sm.u.T[v][blk(xb, xc)], rec, blk(xb, xc), lane);
         }
     }
 }
