@@ -265,10 +265,64 @@ __device__ __forceinline__ void store_tblock(const Blk &Tb, ChunkRec *rec, int b
     st4(&rec->TP[1][bi][r][c0], l);
 }
 
+// Tile b of the prep's stage 1 by one wave: its K K^T part (KK: A of each
+// v-head into LDS) and / or its Q K^T part (KQ: P of each v-head to the
+// records), with bq the q fragments of the tile's t-tile.  after_mma runs
+// once the products have read bq.
+template <int VPW, bool KK, bool KQ, typename F>
+__device__ __forceinline__ void prep_tile(PrepSmem<VPW> &sm, const RecurrentArgs &a, ChunkRec *rec0, int b,
+                                          const bf16x8 (&bq)[DKC / 32], int lane, F &&after_mma) {
+    const int lr = lane & 15, lq = lane >> 4;
+    int bt, bc;
+    tile_of(b, bt, bc);
+    const int t = 16 * bt + lr, i0 = 16 * bc + 4 * lq;
+    f32x4 kk = {0.f, 0.f, 0.f, 0.f}, kq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DKC / 32; ++ks) {
+        const bf16x8 ai = frag(&sm.u.K[0][0], LDK, 16 * bc, 32 * ks, lane);
+        if (KK) {
+            const bf16x8 bk = frag(&sm.u.K[0][0], LDK, 16 * bt, 32 * ks, lane);
+            kk = mma(ai, bk, kk);
+        }
+        if (KQ) kq = mma(ai, bq[ks], kq);
+    }
+    after_mma();
+    const float rk_t = sm.rk[t], rq_t = sm.rq[t];
+#pragma unroll
+    for (int v = 0; v < VPW; ++v) {
+        const float lam_t = sm.lam[v][t], beta_t = sm.beta[v][t];
+        f32x4 av, pv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = i0 + e;
+            const float decay = i <= t ? exp_fast(lam_t - sm.lam[v][i]) : 0.f;
+            av[e] = i < t ? beta_t * rk_t * sm.rk[i] * decay * kk[e] : 0.f;
+            pv[e] = i <= t ? a.scale * rq_t * sm.rk[i] * decay * kq[e] : 0.f;
+        }
+        if (KK) *reinterpret_cast<f32x4 *>(&sm.A[v][b][lr][4 * lq]) = av;
+        if (KQ) {
+            bf16x4 ph, pl;
+            split4(pv, ph, pl);
+            st4(&rec0[v].TP[2][b][lr][4 * lq], ph);
+            st4(&rec0[v].TP[3][b][lr][4 * lq], pl);
+        }
+    }
+}
+
 template <int VPW>
 __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, ChunkRec *recs) {
     constexpr int NT = NTH * VPW, NW = NT / 64;
-    constexpr int GW = NW - VPW;                // waves GW + v: gates and per-token scalars of v-head v
+    // Stage 1's work, the ten lower-triangular tiles of K K^T and Q K^T, is
+    // spread so that no wave has two full tiles more than another: tiles
+    // 0-7 whole, round-robin, and tiles 8 and 9 (both of t-tile 3) split
+    // into their K K^T and Q K^T halves.  The Q K^T halves go to the waves
+    // whose own tile is of t-tile 3 (their q fragments serve again), the
+    // K K^T halves and the gates / per-token scalars to waves of the rest:
+    //   VPW = 2: waves 2, 3 the K K^T halves, 6, 7 the Q K^T halves, 4, 5 the scalars
+    //   VPW = 1: waves 0, 1 the K K^T halves, 2, 3 the Q K^T halves, 1 the scalars
+    constexpr int GW = VPW == 2 ? 4 : 1;        // waves GW + v: gates and per-token scalars of v-head v
+    constexpr int HKK = VPW == 2 ? 2 : 0;       // waves HKK, HKK + 1: the K K^T halves of tiles 8, 9
+    constexpr int HKQ = VPW == 2 ? 6 : 2;       // waves HKQ, HKQ + 1: the Q K^T halves of tiles 8, 9
     __shared__ PrepSmem<VPW> sm;
     const int HV = a.num_v_heads, NP = HV / VPW;
     // head-pair-major, XCD-contiguous: an XCD prepares all chunks of a range
@@ -338,7 +392,7 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
             sm.rq[tok] = a.l2norm ? rsqrtf(sqq + 1e-6f) : 1.f;
         }
     }
-    if (w >= GW) {
+    if (w >= GW && w < GW + VPW) {
         // padded tokens: g = 0 and beta = 0 make them exact no-ops
         const int v = w - GW, h = h0 + v;
         float gg = lane < n ? a.g[(int64_t)(t0 + lane) * HV + h] : 0.f;
@@ -354,7 +408,7 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
     __syncthreads();
 
     // per-token scalars for the scan (wave GW + v for v-head v)
-    if (w >= GW) {
+    if (w >= GW && w < GW + VPW) {
         const int v = w - GW, t = lane;
         ChunkRec *rec = recs + (int64_t)gch * HV + h0 + v;
         const float lam = sm.lam[v][t], lamC = sm.lam[v][CT - 1];
@@ -365,48 +419,24 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
         st_f32(&rec->u2f[t], expf(lamC - lam) * rk);
         st_f32(&rec->gC[t], expf(lamC));
     }
-    // ---- stage 1: the ten lower-triangular tiles (t-tile bt, i-tile bc) of
-    // K K^T and K Q^T, round-robin over the waves, laid out so each lane holds
-    // 4 consecutive i of one row t; per v-head, A (fp32) into its LDS block and
-    // P (hi/lo) to the workspace with 8-byte stores.  The next tile's q loads
-    // go out as soon as this tile's products have read its q.
-    for (int b = w; b < NBLK16; b += NW) {
-        int bt, bc;
-        tile_of(b, bt, bc);
-        const int t = 16 * bt + lr, i0 = 16 * bc + 4 * lq;
-        f32x4 kk = {0.f, 0.f, 0.f, 0.f}, kq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < DKC / 32; ++ks) {
-            const bf16x8 ai = frag(&sm.u.K[0][0], LDK, 16 * bc, 32 * ks, lane);
-            const bf16x8 bk = frag(&sm.u.K[0][0], LDK, 16 * bt, 32 * ks, lane);
-            kk = mma(ai, bk, kk);
-            kq = mma(ai, bq[ks], kq);
-        }
-        if (b + NW < NBLK16) {
-            int nbt, nbc;
-            tile_of(b + NW, nbt, nbc);
-            load_qfrag(bq, a, t0, n, hk, nbt, lr, lq);
-        }
-        const float rk_t = sm.rk[t], rq_t = sm.rq[t];
-#pragma unroll
-        for (int v = 0; v < VPW; ++v) {
-            const float lam_t = sm.lam[v][t], beta_t = sm.beta[v][t];
-            f32x4 av, pv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = i0 + e;
-                const float decay = i <= t ? exp_fast(lam_t - sm.lam[v][i]) : 0.f;
-                av[e] = i < t ? beta_t * rk_t * sm.rk[i] * decay * kk[e] : 0.f;
-                pv[e] = i <= t ? a.scale * rq_t * sm.rk[i] * decay * kq[e] : 0.f;
+    // ---- stage 1: the lower-triangular tiles (t-tile bt, i-tile bc) of
+    // K K^T and K Q^T, laid out so each lane holds 4 consecutive i of one row
+    // t; per v-head, A (fp32) into its LDS block and P (hi/lo) to the
+    // workspace with 8-byte stores.  A wave's next full tile's q loads go out
+    // as soon as this tile's products have read its q.
+    ChunkRec *rec0 = recs + (int64_t)gch * HV + h0;
+    for (int b = w; b < 8; b += NW) {
+        prep_tile<VPW, true, true>(sm, a, rec0, b, bq, lane, [&] {
+            if (b + NW < 8) {
+                int nbt, nbc;
+                tile_of(b + NW, nbt, nbc);
+                load_qfrag(bq, a, t0, n, hk, nbt, lr, lq);
             }
-            *reinterpret_cast<f32x4 *>(&sm.A[v][b][lr][4 * lq]) = av;
-            bf16x4 ph, pl;
-            split4(pv, ph, pl);
-            ChunkRec *rec = recs + (int64_t)gch * HV + h0 + v;
-            st4(&rec->TP[2][b][lr][4 * lq], ph);
-            st4(&rec->TP[3][b][lr][4 * lq], pl);
-        }
+        });
     }
+    auto none = [] {};
+    if (w == HKK || w == HKK + 1) prep_tile<VPW, true, false>(sm, a, rec0, 8 + (w - HKK), bq, lane, none);
+    if (w == HKQ || w == HKQ + 1) prep_tile<VPW, false, true>(sm, a, rec0, 8 + (w - HKQ), bq, lane, none);
     __syncthreads();
 
     // ---- stage 2: per v-head v (waves 4 v .. 4 v + 3), T = (I + A)^-1 block
