@@ -287,17 +287,25 @@ __device__ __forceinline__ void prep_tile(PrepSmem<VPW> &sm, const RecurrentArgs
         if (KQ) kq = mma(ai, bq[ks], kq);
     }
     after_mma();
+    // Every value is computed for all 16 x 16 positions and the triangle is
+    // kept by selects: with the LDS reads and the exponential under a
+    // condition, the compiler branched around each element and waited for
+    // each read on its own.  (Above the diagonal lam_t - lam_i may be
+    // positive and its exponential large or infinite; the select drops it.)
     const float rk_t = sm.rk[t], rq_t = sm.rq[t];
+    const f32x4 rk_i = *reinterpret_cast<const f32x4 *>(&sm.rk[i0]);
 #pragma unroll
     for (int v = 0; v < VPW; ++v) {
-        const float lam_t = sm.lam[v][t], beta_t = sm.beta[v][t];
+        const float lam_t = sm.lam[v][t];
+        const float fa = sm.beta[v][t] * rk_t, fp = a.scale * rq_t;
+        const f32x4 lam_i = *reinterpret_cast<const f32x4 *>(&sm.lam[v][i0]);
         f32x4 av, pv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = i0 + e;
-            const float decay = i <= t ? exp_fast(lam_t - sm.lam[v][i]) : 0.f;
-            av[e] = i < t ? beta_t * rk_t * sm.rk[i] * decay * kk[e] : 0.f;
-            pv[e] = i <= t ? a.scale * rq_t * sm.rk[i] * decay * kq[e] : 0.f;
+            const float wi = rk_i[e] * exp_fast(lam_t - lam_i[e]);     // rk_i exp(L_t - L_i)
+            av[e] = i < t ? fa * wi * kk[e] : 0.f;
+            pv[e] = i <= t ? fp * wi * kq[e] : 0.f;
         }
         if (KK) *reinterpret_cast<f32x4 *>(&sm.A[v][b][lr][4 * lq]) = av;
         if (KQ) {
