@@ -269,6 +269,15 @@ def isolated(seed, reps=64):
                 "stores, %d per lane: the fastest of 1, 4, 16)" % (nb_copy / 2e6, nb_copy / 2e6, u_copy),
         "avg_launch_us": us_copy, "gb_per_s": nb_copy / us_copy / 1e3, "hbm_frac": nb_copy / us_copy / 1e3 / HBM_PEAK_GBS}
     out["conv_varlen"]["frac_of_ceiling"] = out["conv_varlen"]["gb_per_s"] / out["conv_varlen"]["ceiling"]["gb_per_s"]
+    # the same call with 16-token programs (two descriptors per program,
+    # gdn_causal_conv1d_varlen_tiles): same results, 19 rows read per 16 tokens
+    calls = [lambda x=x, y=y: check(lib.gdn_causal_conv1d_varlen_tiles(
+        x.data_ptr(), C, w.data_ptr(), b.data_ptr(), cs.data_ptr(), SLOTS, qsl2_d.data_ptr(), idx2.data_ptr(),
+        hi2.data_ptr(), ch2_d.data_ptr(), len(ch2), y.data_ptr(), C, 2, T2, C, K, 1, 2, sptr), "conv_varlen_tiles")
+        for x, y in sets]
+    out["conv_varlen_16token_programs"] = entry(timed(calls), bytes_conv_varlen(T2, 2, 0, len(ch2)),
+                                                shape="the same in 16-token programs: 128 descriptor pairs x 4 channel tiles",
+                                                buffer_sets=len(sets))
     del sets, calls
 
     # A2 + A3 at the decode shape: 32 sequences, 16 q/k heads, 32 v heads, d = 128

@@ -25,7 +25,7 @@ CONV_CHUNK_TOKENS = 8
 CONV_WIDTH = 4
 
 # every entry point declared in include/gdn.h
-EXPORTS = ("gdn_last_error", "gdn_build_conv_chunks", "gdn_causal_conv1d_varlen",
+EXPORTS = ("gdn_last_error", "gdn_build_conv_chunks", "gdn_causal_conv1d_varlen", "gdn_causal_conv1d_varlen_tiles",
            "gdn_causal_conv1d_update", "gdn_fused_recurrent_decode", "gdn_chunk_gated_delta_rule",
            "gdn_fused_conv_decode", "gdn_chunk_workspace_size", "gdn_chunk_rule_and_fused_decode",
            "gdn_chunk_rule_and_fused_decode_noalloc")
@@ -47,6 +47,8 @@ def _bind(path):
     lib.gdn_build_conv_chunks.argtypes = [P, i32, P, i32, P]
     lib.gdn_causal_conv1d_varlen.argtypes = [P, i64, P, P, P, i32, P, P, P, P, i32, P, i64,
                                              i32, i32, i32, i32, i32, P]
+    lib.gdn_causal_conv1d_varlen_tiles.argtypes = [P, i64, P, P, P, i32, P, P, P, P, i32, P, i64,
+                                                   i32, i32, i32, i32, i32, i32, P]
     lib.gdn_causal_conv1d_update.argtypes = [P, i64, P, P, P, i32, P, P, i64, i32, i32, i32, i32, P]
     lib.gdn_fused_recurrent_decode.argtypes = [P, i64, P, i64, P, i64, P, P, P, i32, P, P, P, P, i64,
                                                i32, i32, i32, i32, i32, i32, f32, i32, P]
@@ -240,13 +242,15 @@ def _check_index(t, n, name, dt):
 
 
 def gdn_causal_conv1d_varlen(x, weight, bias, conv_state, query_start_loc, state_indices,
-                             has_initial_state, chunks, y, silu=True, stream=None):
+                             has_initial_state, chunks, y, silu=True, stream=None, descriptors_per_program=1):
     """Varlen causal conv (width 4) over packed tokens; see gdn.h.
 
     x, y: bf16 [T][C] (strided rows allowed); weight bf16 [C][4]; bias bf16
     [C] or None; conv_state bf16 [slots][3][C]; query_start_loc int32 [S+1];
     state_indices int32 [S]; has_initial_state uint8 [S] or None; chunks
     int32 [n][2] device tensor from gdn_build_conv_chunks (required when T > 0).
+    descriptors_per_program: 1 (8-token programs, gdn_causal_conv1d_varlen)
+    or 2 (16-token programs, gdn_causal_conv1d_varlen_tiles); same results.
     """
     torch = _torch()
     T, C = _check_conv(x, weight, bias, conv_state, y)
@@ -262,12 +266,15 @@ def gdn_causal_conv1d_varlen(x, weight, bias, conv_state, query_start_loc, state
              ("query_start_loc", query_start_loc), ("state_indices", state_indices),
              ("has_initial_state", has_initial_state), ("chunks", chunks), ("y", y)])
     n_chunks = 0 if chunks is None else chunks.shape[0]
-    rc = lib.gdn_causal_conv1d_varlen(
-        _ptr(x), _rows(x, "x"), _ptr(weight), _ptr(bias), _ptr(conv_state), conv_state.shape[0],
-        _ptr(query_start_loc), _ptr(state_indices), _ptr(has_initial_state),
-        _ptr(chunks) if n_chunks else None, n_chunks, _ptr(y), _rows(y, "y"),
-        S, T, C, weight.shape[1], int(bool(silu)), _stream(stream))
-    _check(rc, "gdn_causal_conv1d_varlen")
+    args = (_ptr(x), _rows(x, "x"), _ptr(weight), _ptr(bias), _ptr(conv_state), conv_state.shape[0],
+            _ptr(query_start_loc), _ptr(state_indices), _ptr(has_initial_state),
+            _ptr(chunks) if n_chunks else None, n_chunks, _ptr(y), _rows(y, "y"),
+            S, T, C, weight.shape[1], int(bool(silu)))
+    if descriptors_per_program == 1:
+        _check(lib.gdn_causal_conv1d_varlen(*args, _stream(stream)), "gdn_causal_conv1d_varlen")
+    else:
+        _check(lib.gdn_causal_conv1d_varlen_tiles(*args, int(descriptors_per_program), _stream(stream)),
+               "gdn_causal_conv1d_varlen_tiles")
 
 
 def gdn_causal_conv1d_update(x, weight, bias, conv_state, state_indices, y, silu=True, stream=None):

@@ -96,13 +96,15 @@ GDN_EXPORT int gdn_build_conv_chunks(const int32_t *qsl_host, int32_t num_seqs, 
     return ok();
 }
 
-GDN_EXPORT int gdn_causal_conv1d_varlen(const gdn_bf16 *x, int64_t x_stride, const gdn_bf16 *weight,
-                                        const gdn_bf16 *bias, gdn_bf16 *conv_state, int32_t num_slots,
-                                        const int32_t *query_start_loc, const int32_t *state_indices,
-                                        const uint8_t *has_initial_state, const gdn_conv_chunk *chunks,
-                                        int32_t n_chunks, gdn_bf16 *y, int64_t y_stride, int32_t num_seqs,
-                                        int32_t num_tokens, int32_t channels, int32_t width, int32_t silu,
-                                        void *stream) {
+// validation shared by the varlen conv entry points; fills `a` and sets
+// `launch` when there is work
+static int conv_varlen_args(const gdn_bf16 *x, int64_t x_stride, const gdn_bf16 *weight, const gdn_bf16 *bias,
+                            gdn_bf16 *conv_state, int32_t num_slots, const int32_t *query_start_loc,
+                            const int32_t *state_indices, const uint8_t *has_initial_state,
+                            const gdn_conv_chunk *chunks, int32_t n_chunks, gdn_bf16 *y, int64_t y_stride,
+                            int32_t num_seqs, int32_t num_tokens, int32_t channels, int32_t width, int32_t silu,
+                            gdn::ConvVarlenArgs &a, bool &launch) {
+    launch = false;
     int rc = check_conv_common(x, x_stride, weight, bias, conv_state, num_slots, y, y_stride, num_tokens,
                                channels, width);
     if (rc) return rc;
@@ -126,9 +128,48 @@ GDN_EXPORT int gdn_causal_conv1d_varlen(const gdn_bf16 *x, int64_t x_stride, con
     if ((int64_t)n_chunks < min_chunks)
         return fail(GDN_ERR_INVALID, "%d descriptors cannot cover %d tokens (at least %lld needed)", n_chunks,
                     num_tokens, (long long)min_chunks);
-    gdn::ConvVarlenArgs a{x, x_stride, weight, bias, conv_state, query_start_loc, state_indices,
-                          has_initial_state, chunks, n_chunks, y, y_stride, channels, silu,
-                          num_seqs, num_slots, num_tokens};
+    a = gdn::ConvVarlenArgs{x, x_stride, weight, bias, conv_state, query_start_loc, state_indices,
+                            has_initial_state, chunks, n_chunks, y, y_stride, channels, silu,
+                            num_seqs, num_slots, num_tokens};
+    launch = true;
+    return ok();
+}
+
+GDN_EXPORT int gdn_causal_conv1d_varlen(const gdn_bf16 *x, int64_t x_stride, const gdn_bf16 *weight,
+                                        const gdn_bf16 *bias, gdn_bf16 *conv_state, int32_t num_slots,
+                                        const int32_t *query_start_loc, const int32_t *state_indices,
+                                        const uint8_t *has_initial_state, const gdn_conv_chunk *chunks,
+                                        int32_t n_chunks, gdn_bf16 *y, int64_t y_stride, int32_t num_seqs,
+                                        int32_t num_tokens, int32_t channels, int32_t width, int32_t silu,
+                                        void *stream) {
+    gdn::ConvVarlenArgs a{};
+    bool launch;
+    const int rc = conv_varlen_args(x, x_stride, weight, bias, conv_state, num_slots, query_start_loc,
+                                    state_indices, has_initial_state, chunks, n_chunks, y, y_stride, num_seqs,
+                                    num_tokens, channels, width, silu, a, launch);
+    if (rc || !launch) return rc;
+    return hip_status(gdn::launch_conv_varlen(a, (hipStream_t)stream), "conv varlen launch");
+}
+
+GDN_EXPORT int gdn_causal_conv1d_varlen_tiles(const gdn_bf16 *x, int64_t x_stride, const gdn_bf16 *weight,
+                                              const gdn_bf16 *bias, gdn_bf16 *conv_state, int32_t num_slots,
+                                              const int32_t *query_start_loc, const int32_t *state_indices,
+                                              const uint8_t *has_initial_state, const gdn_conv_chunk *chunks,
+                                              int32_t n_chunks, gdn_bf16 *y, int64_t y_stride, int32_t num_seqs,
+                                              int32_t num_tokens, int32_t channels, int32_t width, int32_t silu,
+                                              int32_t descriptors_per_program, void *stream) {
+    if (descriptors_per_program != 1 && descriptors_per_program != 2)
+        return fail(GDN_ERR_UNSUPPORTED, "descriptors_per_program %d: must be 1 or 2", descriptors_per_program);
+    gdn::ConvVarlenArgs a{};
+    bool launch;
+    const int rc = conv_varlen_args(x, x_stride, weight, bias, conv_state, num_slots, query_start_loc,
+                                    state_indices, has_initial_state, chunks, n_chunks, y, y_stride, num_seqs,
+                                    num_tokens, channels, width, silu, a, launch);
+    if (rc || !launch) return rc;
+    // the 16-token programs address rows with 32-bit byte offsets
+    if (descriptors_per_program == 2 && (x_stride > ((int64_t)1 << 26) || y_stride > ((int64_t)1 << 26)))
+        return fail(GDN_ERR_UNSUPPORTED, "16-token programs need row strides up to 2^26 elements");
+    a.descriptors_per_program = descriptors_per_program;
     return hip_status(gdn::launch_conv_varlen(a, (hipStream_t)stream), "conv varlen launch");
 }
 

@@ -131,6 +131,155 @@ __global__ __launch_bounds__(THREADS) void conv_varlen_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// 16-token programs (two consecutive descriptors per workgroup), page "RTX
+// 5070 Ti: close Qwen3.5-4B TTFT, TPOT, and VRAM gaps vs vLLM", section
+// "Existing evidence" (the multi-token tile arm), applied to the exact 8-token
+// descriptors of page "perf(gdn): dispatch exact causal-conv chunks".  When
+// the pair's second descriptor continues the first (same sequence, next
+// chunk) its halo is the first's last three rows, already in registers: 19
+// rows are read for 16 tokens instead of 22.  The arithmetic of each token is
+// that of conv_varlen_kernel, so the results are bit-identical.
+// ---------------------------------------------------------------------------
+
+// one descriptor of a pair, resolved (ok: processed; a descriptor past the
+// list, naming no sequence of the call, past its sequence's end, or whose
+// slot lies outside the pool is skipped like padding)
+struct ConvDesc {
+    bool ok, first;
+    int seq, chunk, slot, a, end, t0, n;
+};
+
+__device__ __forceinline__ ConvDesc conv_desc(const gdn_conv_chunk *chunks, int ci, int n_chunks,
+                                              const int32_t *qsl, const int32_t *state_indices, int num_seqs,
+                                              int num_slots, int num_tokens) {
+    ConvDesc c;
+    const gdn_conv_chunk d = chunks[min(ci, n_chunks - 1)];
+    const bool bad = ci >= n_chunks || (unsigned)d.seq >= (unsigned)num_seqs || d.chunk < 0;
+    c.seq = bad ? 0 : d.seq;
+    c.chunk = d.chunk;
+    c.slot = state_indices[c.seq];
+    clamp_range(qsl[c.seq], qsl[c.seq + 1], num_tokens, c.a, c.end);
+    c.ok = !bad && (unsigned)c.slot < (unsigned)num_slots && d.chunk < (c.end - c.a + kChunk - 1) / kChunk;
+    c.first = c.ok && d.chunk == 0;
+    c.t0 = c.ok ? c.a + d.chunk * kChunk : 0;       // a skipped one reads row 0 (the call has tokens)
+    c.n = c.ok ? min(kChunk, c.end - c.t0) : 1;
+    return c;
+}
+
+// outputs of one descriptor from its window (halo already masked), and for a
+// sequence's chunk 0 its new slot rows; as in conv_varlen_kernel
+template <bool SILU>
+__device__ __forceinline__ void conv_emit(const ConvTaps &taps, const uint4 (&h)[3], const uint4 (&r)[kChunk],
+                                          const ConvDesc &c, const uint16_t *x, int64_t x_stride,
+                                          uint16_t *conv_state, int channels, uint16_t *y, int64_t y_stride,
+                                          int c0) {
+    if (!c.ok) return;
+    RowPairs pr[kChunk + 2];
+#pragma unroll
+    for (int j = 0; j < kChunk + 2; ++j) {
+        const uint4 &older = j < 3 ? h[j] : r[j - 3];
+        const uint4 &newer = j + 1 < 3 ? h[j + 1] : r[j - 2];
+        pr[j] = row_pairs(older, newer);
+    }
+    const __amdgpu_buffer_rsrc_t y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        y + (int64_t)c.t0 * y_stride, (short)0, c.n * (int)y_stride * 2, kBufferFlags);
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+        const uint4 out = conv_pairs(taps, pr[i], pr[i + 2], SILU);
+        const u32x4 o4 = {out.x, out.y, out.z, out.w};
+        __builtin_amdgcn_raw_buffer_store_b128(o4, y_rsrc, (i * (int)y_stride + c0) * 2, 0, kBufferWriteThrough);
+    }
+    if (c.first) {
+        uint16_t *st = conv_state + (int64_t)c.slot * 3 * channels + c0;
+        const int L = c.end - c.a;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int wi = L + i;
+            const uint4 fromx =
+                *reinterpret_cast<const uint4 *>(x + (int64_t)(c.a + max(wi - 3, 0)) * x_stride + c0);
+            const uint4 old = select4(wi == 0, h[0], select4(wi == 1, h[1], h[2]));
+            *reinterpret_cast<uint4 *>(st + (int64_t)i * channels) = select4(wi >= 3, fromx, old);
+        }
+    }
+}
+
+// One workgroup per (descriptor pair, channel tile).  Every load reads a
+// valid address (as in conv_varlen_kernel); the second descriptor's own halo
+// goes through a buffer resource whose range is zero when the pair is
+// contiguous, so that case reads nothing for it, without a branch.  Row and
+// halo offsets are 32-bit: the launch requires strides up to 2^26.
+template <int THREADS, bool SILU>
+__global__ __launch_bounds__(THREADS) void conv_varlen16_kernel(
+    const uint16_t *__restrict__ x, int64_t x_stride, const uint16_t *__restrict__ weight,
+    const uint16_t *__restrict__ bias, uint16_t *__restrict__ conv_state,
+    const int32_t *__restrict__ qsl, const int32_t *__restrict__ state_indices,
+    const uint8_t *__restrict__ has_init, const gdn_conv_chunk *__restrict__ chunks, int n_chunks,
+    uint16_t *__restrict__ y, int64_t y_stride, int channels, int n_tiles, int num_seqs, int num_slots,
+    int num_tokens) {
+    constexpr int TILE = THREADS * kConvVec;
+    const int work = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int pair = work / n_tiles;
+    const int tile = work - pair * n_tiles;
+    const int c0 = tile * TILE + threadIdx.x * kConvVec;
+    if (c0 >= channels) return;
+    ConvTaps taps;
+    load_taps(taps, weight, bias, c0);
+
+    const ConvDesc d0 = conv_desc(chunks, 2 * pair, n_chunks, qsl, state_indices, num_seqs, num_slots, num_tokens);
+    const ConvDesc d1 = conv_desc(chunks, 2 * pair + 1, n_chunks, qsl, state_indices, num_seqs, num_slots,
+                                  num_tokens);
+    const bool cont = d0.ok && d1.ok && d1.seq == d0.seq && d1.chunk == d0.chunk + 1;
+
+    uint4 h0[3], r0[kChunk], g1[3], r1[kChunk];
+    {
+        const uint16_t *hp = d0.first ? conv_state + (int64_t)d0.slot * 3 * channels + c0
+                                      : x + (int64_t)(d0.ok ? d0.t0 - 3 : 0) * x_stride + c0;
+        const int64_t hs = d0.first ? (int64_t)channels : d0.ok ? x_stride : 0;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) h0[i] = *reinterpret_cast<const uint4 *>(hp + i * hs);
+    }
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+        const uint16_t *p = x + (int64_t)(d0.t0 + min(i, d0.n - 1)) * x_stride + c0;
+        r0[i] = i < kChunk - 3 ? load_stream16(p) : *reinterpret_cast<const uint4 *>(p);
+    }
+    {
+        // the second descriptor's own halo: the slot rows or its 3 preceding x rows
+        const uint16_t *hb = d1.first ? conv_state + (int64_t)d1.slot * 3 * channels
+                                      : x + (int64_t)(d1.ok ? d1.t0 - 3 : 0) * x_stride;
+        const int hs = d1.first ? channels : (int)x_stride;
+        const int range = (cont || !d1.ok) ? 0 : (2 * hs + channels) * 2;
+        const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(hb), (short)0,
+                                                                            range, kBufferFlags);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hr, (i * hs + c0) * 2,
+                                                                                             0, 0));
+            g1[i] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+        const uint16_t *p = x + (int64_t)(d1.t0 + min(i, d1.n - 1)) * x_stride + c0;
+        r1[i] = i < kChunk - 3 ? load_stream16(p) : *reinterpret_cast<const uint4 *>(p);
+    }
+    // has_initial_state, read unconditionally from valid bytes
+    const uint8_t f0 = *(has_init != nullptr ? has_init + d0.seq : reinterpret_cast<const uint8_t *>(chunks));
+    const uint8_t f1 = *(has_init != nullptr ? has_init + d1.seq : reinterpret_cast<const uint8_t *>(chunks));
+    const uint32_t k0 = (d0.first && has_init != nullptr && f0 == 0) ? 0u : ~0u;
+    const uint32_t k1 = (d1.first && has_init != nullptr && f1 == 0) ? 0u : ~0u;
+    uint4 h1[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        h0[i] = make_uint4(h0[i].x & k0, h0[i].y & k0, h0[i].z & k0, h0[i].w & k0);
+        const uint4 own = make_uint4(g1[i].x & k1, g1[i].y & k1, g1[i].z & k1, g1[i].w & k1);
+        h1[i] = select4(cont, r0[kChunk - 3 + i], own);
+    }
+    conv_emit<SILU>(taps, h0, r0, d0, x, x_stride, conv_state, channels, y, y_stride, c0);
+    conv_emit<SILU>(taps, h1, r1, d1, x, x_stride, conv_state, channels, y, y_stride, c0);
+}
+
 __global__ __launch_bounds__(kConvThreads) void conv_update_kernel(
     const uint16_t *__restrict__ x, int64_t x_stride, const uint16_t *__restrict__ weight,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ conv_state,
@@ -180,7 +329,23 @@ hipError_t launch_conv_varlen_t(const ConvVarlenArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_conv_varlen(const ConvVarlenArgs &a, hipStream_t stream) {
-    return launch_conv_varlen_t<kConvThreads>(a, stream);
+    if (a.descriptors_per_program == 1) return launch_conv_varlen_t<kConvThreads>(a, stream);
+    // 16-token programs: one workgroup per (descriptor pair, channel tile)
+    const int n_tiles = (a.channels + kConvTile - 1) / kConvTile;
+    const long long blocks = (long long)((a.n_chunks + 1) / 2) * n_tiles;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (a.silu)
+        hipLaunchKernelGGL((conv_varlen16_kernel<kConvThreads, true>), dim3((unsigned)blocks), dim3(kConvThreads), 0,
+                           stream, a.x, a.x_stride, a.weight, a.bias, a.conv_state, a.qsl, a.state_indices,
+                           a.has_init, a.chunks, a.n_chunks, a.y, a.y_stride, a.channels, n_tiles, a.num_seqs,
+                           a.num_slots, a.num_tokens);
+    else
+        hipLaunchKernelGGL((conv_varlen16_kernel<kConvThreads, false>), dim3((unsigned)blocks), dim3(kConvThreads), 0,
+                           stream, a.x, a.x_stride, a.weight, a.bias, a.conv_state, a.qsl, a.state_indices,
+                           a.has_init, a.chunks, a.n_chunks, a.y, a.y_stride, a.channels, n_tiles, a.num_seqs,
+                           a.num_slots, a.num_tokens);
+    return hipGetLastError();
 }
 
 hipError_t launch_conv_update(const ConvUpdateArgs &a, hipStream_t stream) {

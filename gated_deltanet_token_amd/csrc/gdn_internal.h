@@ -27,6 +27,7 @@ struct ConvVarlenArgs {
     int num_seqs;                // descriptors naming another sequence are skipped
     int num_slots;               // state indices at or past it are skipped
     int num_tokens;              // sequence ends are clamped to it
+    int descriptors_per_program = 1;   // 1: 8-token programs; 2: 16-token programs
 };
 
 struct ConvUpdateArgs {

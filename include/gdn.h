@@ -6,6 +6,8 @@
  *
  *   gdn_build_conv_chunks       host: exact (sequence, 8-token chunk) list
  *   gdn_causal_conv1d_varlen    GPU: width-4 causal conv over packed prefill
+ *   gdn_causal_conv1d_varlen_tiles
+ *                               GPU: the same, 8- or 16-token programs
  *   gdn_causal_conv1d_update    GPU: single-token conv for decode
  *   gdn_fused_recurrent_decode  GPU: gated delta rule over packed tokens
  *   gdn_chunk_gated_delta_rule  GPU: the same rule over prefill tokens,
@@ -158,6 +160,38 @@ int gdn_causal_conv1d_varlen(const gdn_bf16 *x, int64_t x_stride,
                              gdn_bf16 *y, int64_t y_stride,
                              int32_t num_seqs, int32_t num_tokens, int32_t channels,
                              int32_t width, int32_t silu, void *stream);
+
+/*
+ * gdn_causal_conv1d_varlen_tiles -- gdn_causal_conv1d_varlen with a choice of
+ * program size: each program takes descriptors_per_program consecutive
+ * entries of the descriptor list (1: 8-token programs, exactly
+ * gdn_causal_conv1d_varlen; 2: 16-token programs).  The descriptors stay the
+ * exact 8-token ones; when a program's second descriptor continues its first
+ * (same sequence, next chunk), its 3-row halo is the first's last rows, so a
+ * 16-token program reads 19 rows where two 8-token programs read 22.
+ * Results are bit-identical to gdn_causal_conv1d_varlen for every input.
+ *
+ * Sources: page "RTX 5070 Ti: close Qwen3.5-4B TTFT, TPOT, and VRAM gaps vs
+ * vLLM", section "Existing evidence" (the multi-token tile arm of the conv);
+ * page "perf(gdn): dispatch exact causal-conv chunks", section "What changed"
+ * (exact 8-token descriptors).
+ *
+ * Arguments, layouts and errors as gdn_causal_conv1d_varlen, plus:
+ *   descriptors_per_program  1 or 2, else GDN_ERR_UNSUPPORTED; with 2, x_stride
+ *                            and y_stride must be at most 2^26 elements
+ *                            (GDN_ERR_UNSUPPORTED otherwise)
+ */
+int gdn_causal_conv1d_varlen_tiles(const gdn_bf16 *x, int64_t x_stride,
+                                   const gdn_bf16 *weight, const gdn_bf16 *bias,
+                                   gdn_bf16 *conv_state, int32_t num_slots,
+                                   const int32_t *query_start_loc,
+                                   const int32_t *state_indices,
+                                   const uint8_t *has_initial_state,
+                                   const gdn_conv_chunk *chunks, int32_t n_chunks,
+                                   gdn_bf16 *y, int64_t y_stride,
+                                   int32_t num_seqs, int32_t num_tokens, int32_t channels,
+                                   int32_t width, int32_t silu,
+                                   int32_t descriptors_per_program, void *stream);
 
 /*
  * gdn_causal_conv1d_update -- the same conv for one new token per sequence

@@ -113,6 +113,30 @@ def test_conv_varlen_without_tokens_or_descriptors_is_a_no_op():
     assert varlen(ch=None, nch=0, T=0, S=0) == gdn.GDN_OK
 
 
+def varlen_tiles(dpp, **kw):
+    a = dict(x=X, xs=8192, w=W, b=B, cs=CS, slots=64, qsl=QSL, idx=IDX, hi=HI, ch=CH, nch=256,
+             y=Y, ys=8192, S=2, T=2048, C=8192, K=4, silu=1)
+    a.update(kw)
+    return gdn.lib.gdn_causal_conv1d_varlen_tiles(a["x"], a["xs"], a["w"], a["b"], a["cs"], a["slots"], a["qsl"],
+                                                  a["idx"], a["hi"], a["ch"], a["nch"], a["y"], a["ys"], a["S"],
+                                                  a["T"], a["C"], a["K"], a["silu"], dpp, None)
+
+
+@pytest.mark.parametrize("dpp,kw,code", [
+    (0, {}, UNS), (3, {}, UNS), (-1, {}, UNS),
+    (2, dict(x=None), INV), (2, dict(nch=255), INV), (1, dict(ch=None, nch=0), INV),
+    # strides past 2^26 (x or y placed far apart, so they do not overlap)
+    (2, dict(xs=(1 << 26) + 8, y=1 << 44), UNS), (2, dict(ys=(1 << 26) + 8, y=1 << 44), UNS),
+])
+def test_conv_varlen_tiles_validation(dpp, kw, code):
+    assert varlen_tiles(dpp, **kw) == code, gdn.lib.gdn_last_error()
+    assert gdn.lib.gdn_last_error()
+
+
+def test_conv_varlen_tiles_without_tokens_is_a_no_op():
+    assert varlen_tiles(2, ch=None, nch=0, T=0) == gdn.GDN_OK, gdn.lib.gdn_last_error()
+
+
 def update(**kw):
     a = dict(x=X, xs=8192, w=W, b=B, cs=CS, slots=64, idx=IDX, y=Y, ys=8192, B=32, C=8192, K=4, silu=1)
     a.update(kw)
