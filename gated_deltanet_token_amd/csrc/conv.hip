@@ -39,23 +39,35 @@ __global__ __launch_bounds__(THREADS) void conv_varlen_kernel(
     const int ci = work / n_tiles;
     const int tile = work - ci * n_tiles;
     const int c0 = tile * TILE + threadIdx.x * kConvVec;
-    if (c0 >= channels) return;
+    const bool lane_ok = c0 < channels;
 
     // The taps first: they do not depend on the descriptor, and the first
-    // output row needs them, so its wait does not cover the row loads.
+    // output row needs them, so its wait does not cover the row loads.  (A
+    // lane past the channel count reads channel 0's and exits below.)
     ConvTaps taps;
-    load_taps(taps, weight, bias, c0);
+    load_taps(taps, weight, bias, lane_ok ? c0 : 0);
 
-    // A descriptor naming no sequence of the call, and a slot index outside
-    // the pool, are skipped like padding: nothing is read or written for them.
+    // A descriptor naming no sequence of the call, a slot index outside the
+    // pool, and a chunk past its sequence's end are skipped like padding:
+    // nothing is read or written for them.  Every test is made in one exit,
+    // after the slot and the bounds are fetched together (the tests combine
+    // without short-circuit), so the row addresses wait for two dependent
+    // round trips (descriptor, then slot and bounds) rather than one per test.
     const gdn_conv_chunk d = chunks[ci];
     const bool bad = (unsigned)d.seq >= (unsigned)num_seqs || d.chunk < 0;
     const int seq = bad ? 0 : d.seq;
     const int slot = state_indices[seq];
-    if (bad || (unsigned)slot >= (unsigned)num_slots) return;
+    const int lo_raw = qsl[seq], hi_raw = qsl[seq + 1];
+    // (the slot and the bounds issued before either is waited for; every
+    // argument used past the exit fetched before it, with the first ones,
+    // rather than in a round trip of its own after it)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::"s"(x), "s"(weight), "s"(bias), "s"(conv_state), "s"(y), "s"(has_init), "s"(x_stride),
+                 "s"(y_stride), "s"(channels));
     int a, end;
-    clamp_range(qsl[seq], qsl[seq + 1], num_tokens, a, end);
-    if (d.chunk >= (end - a + kChunk - 1) / kChunk) return;
+    clamp_range(lo_raw, hi_raw, num_tokens, a, end);
+    const bool skip = bad | ((unsigned)slot >= (unsigned)num_slots) | (d.chunk >= (end - a + kChunk - 1) / kChunk);
+    if (!lane_ok | skip) return;
     const int t0 = a + d.chunk * kChunk;
     const int n = min(kChunk, end - t0);
 

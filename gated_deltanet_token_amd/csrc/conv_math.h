@@ -62,6 +62,15 @@ __device__ __forceinline__ uint32_t pair_odd(uint32_t older, uint32_t newer) {
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
+// The same product into a new register: the three-operand encoding, so a
+// bias shared by several output rows is not first copied into each row's
+// accumulator (the compiler emits the two-operand form, whose accumulator is
+// also its destination, plus a copy).
+__device__ __forceinline__ float dot2_bf16_3op(uint32_t a, uint32_t b, float c) {
+    float d;
+    asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
 
 // The 8 channels of two consecutive window rows as bf16 pairs (older, newer),
 // channel c in p[c].  An output row uses the pairs of its window rows (0, 1)
@@ -88,7 +97,7 @@ __device__ __forceinline__ uint4 conv_pairs(const ConvTaps &t, const RowPairs &p
     float out[kConvVec];
 #pragma unroll
     for (int c = 0; c < kConvVec; ++c) {
-        float acc = dot2_bf16(p01.p[c], t.w01[c], t.b[c]);
+        float acc = dot2_bf16_3op(p01.p[c], t.w01[c], t.b[c]);
         acc = dot2_bf16(p23.p[c], t.w23[c], acc);
         out[c] = silu ? silu_f32(acc) : acc;
     }
