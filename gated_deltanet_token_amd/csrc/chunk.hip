@@ -265,18 +265,19 @@ __device__ __forceinline__ void store_tblock(const Blk &Tb, ChunkRec *rec, int b
     st4(&rec->TP[1][bi][r][c0], l);
 }
 
-// Tile b of the prep's stage 1 by one wave: its K K^T part (KK: A of each
-// v-head into LDS) and / or its Q K^T part (KQ: P of each v-head to the
-// records), with bq the q fragments of the tile's t-tile.  after_mma runs
-// once the products have read bq.
-template <int VPW, bool KK, bool KQ, typename F>
-__device__ __forceinline__ void prep_tile(PrepSmem<VPW> &sm, const RecurrentArgs &a, ChunkRec *rec0, int b,
-                                          const bf16x8 (&bq)[DKC / 32], int lane, F &&after_mma) {
-    const int lr = lane & 15, lq = lane >> 4;
+// Tile b of the prep's stage 1 by one wave, in two steps: the products
+// (tile_products: its K K^T part KK and / or its Q K^T part KQ, with bq the
+// q fragments of the tile's t-tile), then the element work (tile_elements:
+// A of each v-head into LDS for KK, P of each v-head to the records for KQ).
+// A wave with two tiles forms both tiles' products before the element work
+// of either, so the second tile's LDS reads and products overlap the first
+// tile's instead of following them.
+template <int VPW, bool KK, bool KQ>
+__device__ __forceinline__ void tile_products(PrepSmem<VPW> &sm, int b, const bf16x8 (&bq)[DKC / 32], int lane,
+                                              f32x4 &kk, f32x4 &kq) {
     int bt, bc;
     tile_of(b, bt, bc);
-    const int t = 16 * bt + lr, i0 = 16 * bc + 4 * lq;
-    f32x4 kk = {0.f, 0.f, 0.f, 0.f}, kq = {0.f, 0.f, 0.f, 0.f};
+    kk = kq = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < DKC / 32; ++ks) {
         const bf16x8 ai = frag(&sm.u.K[0][0], LDK, 16 * bc, 32 * ks, lane);
@@ -286,7 +287,15 @@ __device__ __forceinline__ void prep_tile(PrepSmem<VPW> &sm, const RecurrentArgs
         }
         if (KQ) kq = mma(ai, bq[ks], kq);
     }
-    after_mma();
+}
+
+template <int VPW, bool KK, bool KQ>
+__device__ __forceinline__ void tile_elements(PrepSmem<VPW> &sm, const RecurrentArgs &a, ChunkRec *rec0, int b,
+                                              int lane, const f32x4 &kk, const f32x4 &kq) {
+    const int lr = lane & 15, lq = lane >> 4;
+    int bt, bc;
+    tile_of(b, bt, bc);
+    const int t = 16 * bt + lr, i0 = 16 * bc + 4 * lq;
     // Every value is computed for all 16 x 16 positions and the triangle is
     // kept by selects: with the LDS reads and the exponential under a
     // condition, the compiler branched around each element and waited for
@@ -433,18 +442,25 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
     // workspace with 8-byte stores.  A wave's next full tile's q loads go out
     // as soon as this tile's products have read its q.
     ChunkRec *rec0 = recs + (int64_t)gch * HV + h0;
+    const bool half_kk = w == HKK || w == HKK + 1, half_kq = w == HKQ || w == HKQ + 1;
     for (int b = w; b < 8; b += NW) {
-        prep_tile<VPW, true, true>(sm, a, rec0, b, bq, lane, [&] {
-            if (b + NW < 8) {
-                int nbt, nbc;
-                tile_of(b + NW, nbt, nbc);
-                load_qfrag(bq, a, t0, n, hk, nbt, lr, lq);
-            }
-        });
+        f32x4 kk, kq, hk_, hq_;
+        tile_products<VPW, true, true>(sm, b, bq, lane, kk, kq);
+        // a half of tile 8 or 9 after the wave's last whole tile: its
+        // products now, with this tile's (the Q K^T half uses the same q
+        // fragments: this tile is of t-tile 3 too)
+        const bool last = b + NW >= 8;
+        if (last && half_kk) tile_products<VPW, true, false>(sm, 8 + (w - HKK), bq, lane, hk_, hq_);
+        if (last && half_kq) tile_products<VPW, false, true>(sm, 8 + (w - HKQ), bq, lane, hk_, hq_);
+        if (!last) {
+            int nbt, nbc;
+            tile_of(b + NW, nbt, nbc);
+            load_qfrag(bq, a, t0, n, hk, nbt, lr, lq);
+        }
+        tile_elements<VPW, true, true>(sm, a, rec0, b, lane, kk, kq);
+        if (last && half_kk) tile_elements<VPW, true, false>(sm, a, rec0, 8 + (w - HKK), lane, hk_, hq_);
+        if (last && half_kq) tile_elements<VPW, false, true>(sm, a, rec0, 8 + (w - HKQ), lane, hk_, hq_);
     }
-    auto none = [] {};
-    if (w == HKK || w == HKK + 1) prep_tile<VPW, true, false>(sm, a, rec0, 8 + (w - HKK), bq, lane, none);
-    if (w == HKQ || w == HKQ + 1) prep_tile<VPW, false, true>(sm, a, rec0, 8 + (w - HKQ), bq, lane, none);
     __syncthreads();
 
     // ---- stage 2: per v-head v (waves 4 v .. 4 v + 3), T = (I + A)^-1 block
