@@ -468,22 +468,49 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
     {
         const int v = w >> 2, wb = w & 3;
         ChunkRec *rec = recs + (int64_t)gch * HV + h0 + v;
-        if (lane < 16) {
-            // diagonal block wb by forward substitution, lane j owning column
-            // j, swept by columns: once x_i is final, every later row takes
-            // its term at once (the same sums in the same order as row by
-            // row, with independent multiply-adds in each step)
+        {
+            // diagonal block wb by forward substitution on all 64 lanes: lane
+            // (j, g) = (lane % 16, lane / 16) owns rows 4 g .. 4 g + 3 of
+            // column j.  Row group p becomes final in phase p: its lanes take
+            // the terms of their own group's earlier rows, then hand the four
+            // final values to the later groups (an LDS permute), which take
+            // the group's terms.  Every element gets the terms of rows
+            // 0, 1, 2, ... in that order, each as one fused multiply-add:
+            // the same operations as a sweep of one lane per column.
             const Blk &Ad = sm.A[v][blk(wb, wb)];
-            float x[16];
+            const int j = lane & 15, g = lane >> 4;
+            float x[4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = r == lane ? 1.f : 0.f;
+            for (int e = 0; e < 4; ++e) x[e] = 4 * g + e == j ? 1.f : 0.f;
 #pragma unroll
-            for (int i = 0; i < 15; ++i)
+            for (int p = 0; p < 4; ++p) {
+                // this phase's coefficients of the lane's rows, A[4 g + e][4 p .. 4 p + 3]
+                // (read whatever g is, so the reads need not wait for the permute)
+                f32x4 ap[4];
 #pragma unroll
-                for (int r = i + 1; r < 16; ++r) x[r] = __builtin_fmaf(-Ad[r][i], x[i], x[r]);
+                for (int e = 0; e < 4; ++e) ap[e] = *reinterpret_cast<const f32x4 *>(&Ad[4 * g + e][4 * p]);
+                if (g == p) {
+#pragma unroll
+                    for (int e = 1; e < 4; ++e)
+#pragma unroll
+                        for (int f = 0; f < e; ++f) x[e] = __builtin_fmaf(-ap[e][f], x[f], x[e]);
+                }
+                if (p == 3) break;
+                float xp[4];
+#pragma unroll
+                for (int f = 0; f < 4; ++f)
+                    xp[f] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (j + 16 * p),
+                                                                                  __builtin_bit_cast(int, x[f])));
+                if (g > p) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int f = 0; f < 4; ++f) x[e] = __builtin_fmaf(-ap[e][f], xp[f], x[e]);
+                }
+            }
             Blk &Td = sm.u.T[v][blk(wb, wb)];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Td[r][lane] = x[r];
+            for (int e = 0; e < 4; ++e) Td[4 * g + e][j] = x[e];
         }
         __syncthreads();
         store_tblock(sm.u.T[v][blk(wb, wb)], rec, blk(wb, wb), lane);
