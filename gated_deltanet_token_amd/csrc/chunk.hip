@@ -443,7 +443,7 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
     // as soon as this tile's products have read its q.
     ChunkRec *rec0 = recs + (int64_t)gch * HV + h0;
     const bool half_kk = w == HKK || w == HKK + 1, half_kq = w == HKQ || w == HKQ + 1;
-    for (int b = w; b < 8; b += NW) {
+    auto tile = [&](int b) {
         f32x4 kk, kq, hk_, hq_;
         tile_products<VPW, true, true>(sm, b, bq, lane, kk, kq);
         // a half of tile 8 or 9 after the wave's last whole tile: its
@@ -460,6 +460,16 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
         tile_elements<VPW, true, true>(sm, a, rec0, b, lane, kk, kq);
         if (last && half_kk) tile_elements<VPW, true, false>(sm, a, rec0, 8 + (w - HKK), lane, hk_, hq_);
         if (last && half_kq) tile_elements<VPW, false, true>(sm, a, rec0, 8 + (w - HKQ), lane, hk_, hq_);
+    };
+    // With eight waves each has exactly one whole tile, written without a
+    // loop: a loop the compiler cannot prove runs makes it count the q
+    // fragment loads as possibly outstanding after it, and it then waits for
+    // every memory operation, this stage's record stores included, before
+    // it reuses their registers.
+    if constexpr (NW == 8) {
+        tile(w);
+    } else {
+        for (int b = w; b < 8; b += NW) tile(b);
     }
     __syncthreads();
 
