@@ -527,12 +527,17 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
         // The off-diagonal blocks as 2 x 2 block inverses of the 32 x 32
         // halves T1 = (T00, T10, T11) and T2 = (T22, T32, T33), then the
         // lower-left half -T2 A21 T1 (A21 = A20, A21, A30, A31):
-        //   level 1: T10 = -T11 A10 T00 (wave 0), T32 = -T33 A32 T22 (wave 1)
-        //   level 2: X = A21 T1, one block per wave, written over A21
+        //   level 1: T10 = -T11 A10 T00 (wave 0), T32 = -T33 A32 T22 (wave 1);
+        //            meanwhile waves 2 and 3 (b = 2, 3) form the parts of
+        //            X_b0 = A_b0 T00 + A_b1 T10 and X_b1 = A_b1 T11 that need
+        //            no level-1 block: A_b0 T00 and X_b1
+        //   level 2: X_b0 += A_b1 T10 (waves 2, 3); X written over A21
         //   level 3: T20 = -T22 X20, T21 = -T22 X21, T30 = -(T32 X20 + T33 X30),
         //            T31 = -(T32 X21 + T33 X31), one block per wave
-        // Every product is a 16 x 16 fp32 block product on the matrix cores;
-        // the longest chain is six of them.
+        // Every product is a 16 x 16 fp32 block product on the matrix cores,
+        // each block's terms summed in the same order as a block-column walk;
+        // the longest chain is five of them.
+        f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};   // waves 2, 3: X_b0, X_b1
         if (wb < 2) {
             const int b = wb == 0 ? 1 : 3, c = b - 1;       // T10 or T32
             f32x4 m = {0.f, 0.f, 0.f, 0.f};
@@ -542,18 +547,19 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
             t = mm16(sm.u.T[v][blk(b, b)], sm.u.T[v][blk(b, c)], t, lane);
             put16(sm.u.T[v][blk(b, c)], t, -1.f, lane);
             store_tblock(sm.u.T[v][blk(b, c)], rec, blk(b, c), lane);
+        } else {
+            x0 = mm16(sm.A[v][blk(wb, 0)], sm.u.T[v][blk(0, 0)], x0, lane);
+            x1 = mm16(sm.A[v][blk(wb, 1)], sm.u.T[v][blk(1, 1)], x1, lane);
+        }
+        __syncthreads();                                     // T10 final
+        if (wb >= 2) x0 = mm16(sm.A[v][blk(wb, 1)], sm.u.T[v][blk(1, 0)], x0, lane);
+        __syncthreads();                                     // every A_b0, A_b1 read before any is overwritten
+        if (wb >= 2) {
+            put16(sm.A[v][blk(wb, 0)], x0, 1.f, lane);
+            put16(sm.A[v][blk(wb, 1)], x1, 1.f, lane);
         }
         __syncthreads();
         const int xb = 2 + (wb >> 1), xc = wb & 1;          // this wave's block (xb, xc) of the lower-left half
-        {
-            // X_bc = A_b0 T_0c + A_b1 T_1c (T_01 = 0)
-            f32x4 x = {0.f, 0.f, 0.f, 0.f};
-            if (xc == 0) x = mm16(sm.A[v][blk(xb, 0)], sm.u.T[v][blk(0, 0)], x, lane);
-            x = mm16(sm.A[v][blk(xb, 1)], sm.u.T[v][blk(1, xc)], x, lane);
-            __syncthreads();                                 // every A_b0, A_b1 read before any is overwritten
-            put16(sm.A[v][blk(xb, xc)], x, 1.f, lane);
-        }
-        __syncthreads();
         {
             // T_bc = -(T_b2 X_2c + T_b3 X_3c) (T_23 = 0)
             f32x4 t = {0.f, 0.f, 0.f, 0.f};
