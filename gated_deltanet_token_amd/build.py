@@ -38,6 +38,12 @@ CFLAGS = [
     # matrix-core results in ordinary VGPRs: the chunkwise scan's accumulators
     # feed vector arithmetic directly, with no accumulator-register copies
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # the first 14 dwords of a kernel's arguments arrive in SGPRs at wave
+    # launch (kernarg preloading), so a kernel's first dependent fetch (a slot
+    # index, a descriptor) need not wait for its arguments' load; kernels put
+    # the arguments of that chain first.  (A kernel entry also carries the
+    # loads, skipped by firmware that preloads.)
+    "-mllvm", "-amdgpu-kernarg-preload-count=14",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -327,7 +327,22 @@ __device__ __forceinline__ void tile_elements(PrepSmem<VPW> &sm, const Recurrent
 }
 
 template <int VPW>
-__global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, ChunkRec *recs) {
+__global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(const int32_t *qsl, const uint16_t *k,
+                                                                 const uint16_t *q, int64_t k_stride,
+                                                                 int64_t q_stride, int num_seqs, int num_tokens,
+                                                                 int num_v_heads, int n_blocks,
+                                                                 RecurrentArgs a_in, ChunkRec *recs) {
+    // the chunk lookup's and the row loads' arguments, also passed ahead of
+    // the struct: the first 14 dwords arrive preloaded in SGPRs
+    RecurrentArgs a = a_in;
+    a.qsl = qsl;
+    a.k = k;
+    a.q = q;
+    a.k_stride = k_stride;
+    a.q_stride = q_stride;
+    a.num_seqs = num_seqs;
+    a.num_tokens = num_tokens;
+    a.num_v_heads = num_v_heads;
     constexpr int NT = NTH * VPW, NW = NT / 64;
     // Stage 1's work, the ten lower-triangular tiles of K K^T and Q K^T, is
     // spread so that no wave has two full tiles more than another: tiles
@@ -345,8 +360,8 @@ __global__ __launch_bounds__(NTH * VPW) void chunk_prep_kernel(RecurrentArgs a, 
     // head-pair-major, XCD-contiguous: an XCD prepares all chunks of a range
     // of v-heads, the heads whose scan workgroups it also runs, so the scan
     // finds the records in its own L2
-    const int work = xcd_contiguous(blockIdx.x, gridDim.x);
-    const int mcg = gridDim.x / NP;             // chunks the grid covers (an upper bound)
+    const int work = xcd_contiguous(blockIdx.x, n_blocks);
+    const int mcg = n_blocks / NP;              // chunks the grid covers (an upper bound)
     const int h0 = (work / mcg) * VPW;          // the workgroup's first v-head
     const int gch = work % mcg;                 // global chunk index
     int s, j, lo, hi;                           // (sequence, chunk within it, its tokens)
@@ -1005,10 +1020,13 @@ ChunkLaunch chunk_launch(const RecurrentArgs &a, void *workspace, int num_tokens
 hipError_t launch_prep(const RecurrentArgs &a, const ChunkLaunch &c, hipStream_t stream) {
     // two v-heads per prep workgroup whenever the v-heads of a q/k head pair up
     if ((a.num_v_heads / a.num_k_heads) % 2 == 0)
-        hipLaunchKernelGGL(chunk_prep_kernel<2>, dim3((unsigned)(c.prep_blocks / 2)), dim3(2 * NTH), 0, stream, a,
-                           c.recs);
+        hipLaunchKernelGGL(chunk_prep_kernel<2>, dim3((unsigned)(c.prep_blocks / 2)), dim3(2 * NTH), 0, stream, a.qsl,
+                           a.k, a.q, a.k_stride, a.q_stride, a.num_seqs, a.num_tokens, a.num_v_heads,
+                           (int)(c.prep_blocks / 2), a, c.recs);
     else
-        hipLaunchKernelGGL(chunk_prep_kernel<1>, dim3((unsigned)c.prep_blocks), dim3(NTH), 0, stream, a, c.recs);
+        hipLaunchKernelGGL(chunk_prep_kernel<1>, dim3((unsigned)c.prep_blocks), dim3(NTH), 0, stream, a.qsl, a.k, a.q,
+                           a.k_stride, a.q_stride, a.num_seqs, a.num_tokens, a.num_v_heads, (int)c.prep_blocks, a,
+                           c.recs);
     return hipGetLastError();
 }
 

@@ -23,19 +23,22 @@ constexpr int kConvThreads = 256;                       // 4 waves
 constexpr int kConvTile = kConvThreads * kConvVec;      // 2048 channels
 constexpr int kChunk = 8;                               // tokens per descriptor
 
+// The arguments of the descriptor chain come first: the first 14 dwords
+// arrive preloaded in SGPRs, and the grid size is one of them (gridDim would
+// be a load from the dispatch's hidden arguments).
 template <int THREADS, bool SILU, bool WT>
 __global__ __launch_bounds__(THREADS) void conv_varlen_kernel(
-    const uint16_t *__restrict__ x, int64_t x_stride, const uint16_t *__restrict__ weight,
-    const uint16_t *__restrict__ bias, uint16_t *__restrict__ conv_state,
-    const int32_t *__restrict__ qsl, const int32_t *__restrict__ state_indices,
-    const uint8_t *__restrict__ has_init, const gdn_conv_chunk *__restrict__ chunks,
-    uint16_t *__restrict__ y, int64_t y_stride, int channels, int n_tiles, int num_seqs, int num_slots,
-    int num_tokens) {
+    const gdn_conv_chunk *__restrict__ chunks, const int32_t *__restrict__ qsl,
+    const int32_t *__restrict__ state_indices, const uint16_t *__restrict__ weight, int n_tiles, int num_seqs,
+    int num_slots, int num_tokens, int channels, int n_blocks,
+    const uint16_t *__restrict__ bias, const uint16_t *__restrict__ x, int64_t x_stride,
+    const uint8_t *__restrict__ has_init, uint16_t *__restrict__ conv_state,
+    uint16_t *__restrict__ y, int64_t y_stride) {
     constexpr int TILE = THREADS * kConvVec;
     // Chunk-major and XCD-contiguous: each XCD takes one contiguous range of
     // (descriptor, channel tile) items, so a chunk's halo rows are rows its
     // neighbouring chunk fetched into the same L2.
-    const int work = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int work = xcd_contiguous(blockIdx.x, n_blocks);
     const int ci = work / n_tiles;
     const int tile = work - ci * n_tiles;
     const int c0 = tile * TILE + threadIdx.x * kConvVec;
@@ -292,11 +295,13 @@ __global__ __launch_bounds__(THREADS) void conv_varlen16_kernel(
     conv_emit<SILU>(taps, h1, r1, d1, x, x_stride, conv_state, channels, y, y_stride, c0);
 }
 
+// (the slot lookup's and the window's arguments first: the first 14 dwords
+// arrive preloaded in SGPRs)
 __global__ __launch_bounds__(kConvThreads) void conv_update_kernel(
-    const uint16_t *__restrict__ x, int64_t x_stride, const uint16_t *__restrict__ weight,
-    const uint16_t *__restrict__ bias, uint16_t *__restrict__ conv_state,
-    const int32_t *__restrict__ state_indices, uint16_t *__restrict__ y, int64_t y_stride,
-    int channels, int n_tiles, int silu, int num_slots) {
+    const int32_t *__restrict__ state_indices, int n_tiles, int num_slots, uint16_t *__restrict__ conv_state,
+    const uint16_t *__restrict__ x, int64_t x_stride, int channels, int silu,
+    const uint16_t *__restrict__ weight, const uint16_t *__restrict__ bias, uint16_t *__restrict__ y,
+    int64_t y_stride) {
     const int b = blockIdx.x / n_tiles;
     const int tile = blockIdx.x - b * n_tiles;
     const int slot = state_indices[b];
@@ -326,9 +331,9 @@ hipError_t launch_conv_varlen_t(const ConvVarlenArgs &a, hipStream_t stream) {
     // the write-through path addresses the chunk's 8 rows with 32-bit byte offsets
     const bool wt = a.y_stride <= ((int64_t)1 << 26);
     auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(THREADS), 0, stream, a.x, a.x_stride, a.weight,
-                           a.bias, a.conv_state, a.qsl, a.state_indices, a.has_init, a.chunks, a.y, a.y_stride,
-                           a.channels, n_tiles, a.num_seqs, a.num_slots, a.num_tokens);
+        hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(THREADS), 0, stream, a.chunks, a.qsl,
+                           a.state_indices, a.weight, n_tiles, a.num_seqs, a.num_slots, a.num_tokens, a.channels,
+                           (int)blocks, a.bias, a.x, a.x_stride, a.has_init, a.conv_state, a.y, a.y_stride);
     };
     if (a.silu) {
         if (wt) go(conv_varlen_kernel<THREADS, true, true>);
@@ -366,8 +371,8 @@ hipError_t launch_conv_update(const ConvUpdateArgs &a, hipStream_t stream) {
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(conv_update_kernel, dim3((unsigned)blocks), dim3(kConvThreads), 0, stream,
-                       a.x, a.x_stride, a.weight, a.bias, a.conv_state, a.state_indices, a.y,
-                       a.y_stride, a.channels, n_tiles, a.silu, a.num_slots);
+                       a.state_indices, n_tiles, a.num_slots, a.conv_state, a.x, a.x_stride, a.channels, a.silu,
+                       a.weight, a.bias, a.y, a.y_stride);
     return hipGetLastError();
 }
 

