@@ -43,7 +43,7 @@ def _flags(r, n, p):
 
 
 CONV_CASES = []
-for _ in range(24):
+for _ in range(48):
     lens = _lens(_R, 6, 400)
     C = 8 * int(_R.integers(1, 700))               # 8 .. 5592 channels: partial last tile
     CONV_CASES.append(dict(lens=lens, C=C, hi=_flags(_R, len(lens), 0.6), pad=_flags(_R, len(lens), 0.2),
@@ -51,7 +51,7 @@ for _ in range(24):
                            xpad=8 * int(_R.integers(0, 4)), seed=int(_R.integers(1 << 30))))
 
 CHUNK_CASES = []
-for _ in range(24):
+for _ in range(48):
     lens = _lens(_R, 5, 450)
     HK = int(_R.choice([1, 2, 4]))
     HV = HK * int(_R.choice([1, 2, 3, 4]))
@@ -60,7 +60,7 @@ for _ in range(24):
                             scale=float(_R.choice([1.0, 0.0884, 0.5])), seed=int(_R.integers(1 << 30))))
 
 DECODE_CASES = []
-for _ in range(16):
+for _ in range(32):
     HK = int(_R.choice([1, 2, 4, 8]))
     HV = HK * int(_R.choice([1, 2, 4]))
     B = int(_R.integers(1, 41))
@@ -69,7 +69,7 @@ for _ in range(16):
                              scale=float(_R.choice([1.0, 0.25])), seed=int(_R.integers(1 << 30))))
 
 MIXED_CASES = []
-for _ in range(12):
+for _ in range(24):
     lens = _lens(_R, 4, 450)
     HK = int(_R.choice([1, 2, 4]))
     HV = HK * int(_R.choice([1, 2, 4]))
